@@ -1,0 +1,143 @@
+"""Two-cache layer state, chunked prefill and decode (test infrastructure).
+
+What is followed:
+  * each layer keeps two KV caches -- a full one for retrieval heads and one
+    holding only sink and recent tokens for streaming heads; the new token's
+    Q/K/V are split along the head axis, each block attends separately, and
+    the outputs are concatenated along heads -- xllm-io review, section 三
+    推理流程 (解码阶段);
+  * prefill runs in fixed-length chunks that fill both caches; streaming heads
+    need linear time and constant memory -- xllm-io review, section 三
+    (预填充阶段); paperlayer summary, section 2 (Chunked Pre-filling).
+
+Readings: the streaming cache is a ring of S + R slots; position p is stored
+in slot p when p < S, else in slot S + ((p - S) mod R), and writes happen in
+position order, so a later position overwrites an earlier one in its slot.
+A decode step is a chunk of one token (append, then attend: the new token is
+among its own keys). Keys keep their absolute positions; masks are taken on
+those positions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import masked_attention
+from .int4 import quantize_int4_g32, dequantize_int4_g32
+
+
+def ring_slot(p: int, sink: int, recent: int) -> int:
+    return p if p < sink else sink + (p - sink) % recent
+
+
+def ring_positions_after(n_tokens: int, sink: int, recent: int):
+    """Simulate position-ordered writes of positions 0..n-1 into the ring and
+    return slot -> position (-1 = never written)."""
+    slots = [-1] * (sink + recent)
+    for p in range(n_tokens):
+        slots[ring_slot(p, sink, recent)] = p
+    return slots
+
+
+class OracleLayer:
+    """One attention layer's caches in the caller's head order.
+
+    retrieval_mask [Hkv]: nonzero = retrieval head. int4=True stores the
+    retrieval cache with the 4-bit group encoding of ``oracle.int4`` and
+    attends over the dequantised values.
+    """
+
+    def __init__(self, n_q_heads, n_kv_heads, head_dim, retrieval_mask, scale,
+                 sink=16, recent=64, int4=False):
+        self.Hq, self.Hkv, self.D = n_q_heads, n_kv_heads, head_dim
+        self.G = n_q_heads // n_kv_heads
+        self.mask = [int(m) != 0 for m in retrieval_mask]
+        self.scale, self.S, self.R = scale, sink, recent
+        self.int4 = int4
+        self.n = 0
+        # retrieval heads: list of per-token rows (values the attention reads)
+        self.full_k = {h: [] for h in range(n_kv_heads) if self.mask[h]}
+        self.full_v = {h: [] for h in range(n_kv_heads) if self.mask[h]}
+        # int4 encodings kept for byte-level comparison: per head lists of (codes, s, z)
+        self.enc_k = {h: [] for h in self.full_k}
+        self.enc_v = {h: [] for h in self.full_k}
+        # streaming heads: ring slots holding (position, k row, v row)
+        self.ring = {h: [None] * (sink + recent) for h in range(n_kv_heads) if not self.mask[h]}
+
+    # -- caches --------------------------------------------------------------
+    def _store_retrieval(self, h, k_rows, v_rows):
+        if self.int4:
+            ck, sk, zk = quantize_int4_g32(k_rows)
+            cv, sv, zv = quantize_int4_g32(v_rows)
+            self.enc_k[h].append((ck, sk, zk))
+            self.enc_v[h].append((cv, sv, zv))
+            k_rows = dequantize_int4_g32(ck, sk, zk)
+            v_rows = dequantize_int4_g32(cv, sv, zv)
+        self.full_k[h].extend(np.asarray(k_rows, np.float64))
+        self.full_v[h].extend(np.asarray(v_rows, np.float64))
+
+    def append(self, k, v):
+        """Append tokens n..n+T-1 to both caches (no attention). k/v [T,Hkv,D]."""
+        k = np.asarray(k)
+        v = np.asarray(v)
+        T = k.shape[0]
+        for h in range(self.Hkv):
+            if self.mask[h]:
+                self._store_retrieval(h, k[:, h], v[:, h])
+            else:
+                for t in range(T):
+                    p = self.n + t
+                    self.ring[h][ring_slot(p, self.S, self.R)] = (
+                        p, np.asarray(k[t, h], np.float64), np.asarray(v[t, h], np.float64))
+        self.n += T
+
+    def ring_contents(self, h):
+        """slot -> position for streaming head h (-1 = empty)."""
+        return [-1 if e is None else e[0] for e in self.ring[h]]
+
+    # -- attention -------------------------------------------------------------
+    def prefill_chunk(self, q, k, v, rows=None):
+        """Chunk at positions n..n+T-1: q [T,Hq,D], k/v [T,Hkv,D] -> out [T,Hq,D].
+
+        Retrieval heads attend causally over the full cache plus the chunk;
+        streaming heads attend under the Lambda mask over the ring as it was
+        before the chunk plus the chunk itself. Both caches are then updated.
+        ``rows`` restricts the query rows computed (others NaN)."""
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        T = q.shape[0]
+        chunk_pos = np.arange(self.n, self.n + T)
+        rows = np.arange(T) if rows is None else np.asarray(rows)
+        out = np.full((T, self.Hq, self.D), np.nan)
+        for kvh in range(self.Hkv):
+            if self.mask[kvh]:
+                if self.int4:
+                    ck, sk, zk = quantize_int4_g32(k[:, kvh])
+                    cv, sv, zv = quantize_int4_g32(v[:, kvh])
+                    kc = dequantize_int4_g32(ck, sk, zk).astype(np.float64)
+                    vc = dequantize_int4_g32(cv, sv, zv).astype(np.float64)
+                else:
+                    kc, vc = k[:, kvh], v[:, kvh]
+                old_k = np.array(self.full_k[kvh]).reshape(-1, self.D)
+                old_v = np.array(self.full_v[kvh]).reshape(-1, self.D)
+                keys = np.concatenate([old_k, kc])
+                vals = np.concatenate([old_v, vc])
+                k_pos = np.arange(self.n + T)
+                kind = "full"
+            else:
+                held = [e for e in self.ring[kvh] if e is not None]
+                keys = np.array([e[1] for e in held] + list(k[:, kvh])).reshape(-1, self.D)
+                vals = np.array([e[2] for e in held] + list(v[:, kvh])).reshape(-1, self.D)
+                k_pos = np.array([e[0] for e in held] + list(chunk_pos))
+                kind = "streaming"
+            for g in range(self.G):
+                h = kvh * self.G + g
+                out[rows, h] = masked_attention(q[rows, h], keys, vals, chunk_pos[rows], k_pos,
+                                                self.scale, kind, self.S, self.R)
+        self.append(k, v)
+        return out
+
+    def decode(self, q, k, v):
+        """One new token: q [Hq,D], k/v [Hkv,D] -> out [Hq,D]."""
+        return self.prefill_chunk(np.asarray(q)[None], np.asarray(k)[None],
+                                  np.asarray(v)[None])[0]
