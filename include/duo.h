@@ -1,0 +1,175 @@
+/*
+ * duo.h -- C ABI of the DuoAttention head-split attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2410.10819) splits a layer's attention heads into
+ * retrieval heads, which keep a full KV cache and run full causal softmax
+ * attention, and streaming heads, which keep only the first `sink` tokens
+ * and the most recent `recent` tokens and run attention under the
+ * Lambda-shaped mask (xllm-io review "DuoAttention: Efficient Long-Context
+ * LLM Inference with Retrieval and Streaming Heads", section 三 技术架构:
+ * 整体框架 and 核心公式). Each layer holds two caches; Q/K/V of new tokens are
+ * split along the head axis, each block attends separately and the outputs
+ * are concatenated along heads (same page, section 三 推理流程). Prefill runs
+ * in fixed-length chunks that fill both caches (same page, section 三
+ * 预填充阶段; paperlayer summary of arXiv 2410.10819v1, section 2 Chunked
+ * Pre-filling). Heads arrive pre-reordered so that retrieval heads form the
+ * first contiguous block (xllm-io review, section 三 模型部署优化), and the
+ * identification forward blends both attentions with one gate per KV head
+ * (xllm-io review, section 三 核心公式; paperlayer summary, section 2).
+ *
+ * Conventions for every call:
+ *   - Device pointers are plain HIP device addresses. The caller owns every
+ *     device buffer (activations, both caches, the workspace); the library
+ *     never allocates device memory. It allocates only the small host object
+ *     behind duo_layer*, which duo_layer_destroy frees.
+ *   - Activations are token-major: q and out are [B, T, Hq, D], k and v are
+ *     [B, T, Hkv, D], densely packed. Query head h reads KV head h / G with
+ *     G = Hq / Hkv. KV heads [0, Hr) are retrieval heads and [Hr, Hkv) are
+ *     streaming heads, so query heads [0, Hr*G) are retrieval heads.
+ *   - q and out are bf16. k and v are bf16 or fp16 (kv_dtype).
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     No call synchronises the device. The token count is tracked on the
+ *     host. A duo_layer must not be used from two threads at once, and calls
+ *     on one layer must be ordered (same stream, or caller-side events).
+ *   - Every call validates its arguments on the host first. On any error it
+ *     returns a status other than DUO_OK, enqueues nothing and leaves the
+ *     layer state (token count, caches) unchanged. No C++ exception crosses
+ *     this interface. DUO_ERR_HIP reports a failed launch; an earlier
+ *     asynchronous device fault may surface there.
+ *   - Pointers must be 16-byte aligned (DUO_ERR_LAYOUT otherwise).
+ */
+#ifndef DUO_H_
+#define DUO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DUO_OK = 0,
+  DUO_ERR_INVALID_ARG = 1, /* null pointer, bad size or count */
+  DUO_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim 96) */
+  DUO_ERR_LAYOUT = 3,      /* misaligned pointer, non-contiguous head mask */
+  DUO_ERR_CAPACITY = 4,    /* retrieval cache would overflow */
+  DUO_ERR_HIP = 5          /* a HIP launch or API call failed */
+} duo_status;
+
+typedef enum {
+  DUO_BF16 = 0,
+  DUO_FP16 = 1,
+  /* 4-bit codes per channel with one fp16 scale and one fp16 zero-point per
+   * token, head and group of 32 channels (retrieval cache only). */
+  DUO_INT4_G32 = 2
+} duo_dtype;
+
+typedef struct {
+  int32_t batch;                /* B >= 1; every sequence has the same length */
+  int32_t n_q_heads;            /* Hq, a multiple of n_kv_heads, Hq/Hkv <= 8 */
+  int32_t n_kv_heads;           /* Hkv >= 1 */
+  int32_t head_dim;             /* D: 64 or 128 */
+  int32_t n_retrieval_kv_heads; /* Hr in [0, Hkv]: KV heads [0,Hr) are retrieval */
+  int32_t sink;                 /* S >= 0 attention-sink tokens (16 at deployment) */
+  int32_t recent;               /* R >= 1 recent tokens incl. the query (64) */
+  int64_t retrieval_capacity;   /* max tokens held by the retrieval cache */
+  duo_dtype kv_dtype;           /* dtype of k/v inputs and of the ring: BF16 | FP16 */
+  duo_dtype retrieval_dtype;    /* kv_dtype, or INT4_G32 */
+  float softmax_scale;          /* multiplies q.k before the softmax */
+} duo_layer_desc;
+
+/* Byte offsets of the arrays inside the caller-provided buffers.
+ * Retrieval buffer, kv_dtype cache:
+ *   K  [B][Hr][cap][D] elements at k_offset, V likewise at v_offset.
+ * Retrieval buffer, INT4_G32 cache:
+ *   K codes [B][Hr][cap][D/2] bytes at k_offset (byte b of a row holds
+ *   channel 2b in its low nibble and 2b+1 in its high nibble), V codes at
+ *   v_offset, K scale/zero [B][Hr][cap][D/32][2] fp16 (scale, zero) at
+ *   k_sz_offset, V at v_sz_offset.
+ * Streaming buffer: ring K [B][Hs][S+R][D] kv_dtype at ring_k_offset, ring V
+ *   at ring_v_offset, Hs = Hkv - Hr. Token position p lives in slot p if
+ *   p < S, else in slot S + ((p - S) mod R).
+ * Workspace: internal (split-K partials and arrival counters). */
+typedef struct {
+  size_t retrieval_bytes, streaming_bytes, workspace_bytes;
+  size_t k_offset, v_offset, k_sz_offset, v_sz_offset;
+  size_t ring_k_offset, ring_v_offset;
+} duo_layout;
+
+typedef struct duo_layer duo_layer; /* opaque host object */
+
+/* Sizes and offsets of the buffers a layer needs. Host-only; no HIP call.
+ * Errors: DUO_ERR_INVALID_ARG for a null pointer or a bad descriptor,
+ * DUO_ERR_UNSUPPORTED for an unsupported head_dim, group size or dtype. */
+duo_status duo_layer_layout(const duo_layer_desc* desc, duo_layout* layout);
+
+/* Attach a layer to caller-owned device buffers of at least the sizes
+ * duo_layer_layout reports (all 256-byte aligned). `n_tokens_existing`
+ * tokens are taken to be already cached (0 for a fresh layer; a resumed
+ * layer passes its previous count). The workspace is zero-filled on
+ * `stream`. On success *out receives a new handle. */
+duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* desc, void* retrieval_buf,
+                          void* streaming_buf, void* workspace, int64_t n_tokens_existing,
+                          hipStream_t stream);
+
+/* Free the host object (never the caller's buffers). Null is accepted. */
+duo_status duo_layer_destroy(duo_layer* layer);
+
+/* Tokens currently cached by the layer (host counter), or -1 for null. */
+int64_t duo_layer_tokens(const duo_layer* layer);
+
+/* Append `n_tokens` >= 1 tokens of K/V ([B, n_tokens, Hkv, D], kv_dtype)
+ * at positions [n, n + n_tokens) without attending: retrieval heads write
+ * their cache rows (quantising them for INT4_G32), streaming heads write the
+ * ring slots of the positions that survive (the sinks and the last `recent`).
+ * Used to fill a context. DUO_ERR_CAPACITY if n + n_tokens > capacity. */
+duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t n_tokens,
+                         hipStream_t stream);
+
+/* Chunked prefill of `chunk_len` >= 1 tokens at positions [n, n+chunk_len):
+ * q [B, chunk_len, Hq, D] bf16, k/v [B, chunk_len, Hkv, D]. Retrieval heads
+ * append the chunk to their cache and attend causally over positions
+ * [0, n+chunk_len); streaming heads attend under the Lambda mask over the ring
+ * as it was before the chunk plus the chunk, then the ring is updated.
+ * Writes out [B, chunk_len, Hq, D] bf16 and advances the token count. */
+duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,
+                             int32_t chunk_len, void* out, hipStream_t stream);
+
+/* One decode step at position n: q [B, 1, Hq, D] bf16, k_new/v_new
+ * [B, 1, Hkv, D]. The new token is appended to both caches, then every head
+ * attends (retrieval: positions [0, n]; streaming: the sinks and the last
+ * `recent` positions, the new one included). Writes out [B, 1, Hq, D] bf16. */
+duo_status duo_decode(duo_layer* layer, const void* q, const void* k_new, const void* v_new,
+                      void* out, hipStream_t stream);
+
+/* Stateless gate-blended forward used for head identification:
+ * out_h = alpha[h/G] * full_h + (1 - alpha[h/G]) * streaming_h over one
+ * sequence of `seq_len` tokens. q [B, T, Hq, D] bf16, k/v [B, T, Hkv, D]
+ * (kv_dtype must be BF16), alpha [Hkv] fp32 on the device; the descriptor's
+ * retrieval fields are ignored. */
+duo_status duo_mixed_forward(const duo_layer_desc* desc, const void* q, const void* k,
+                             const void* v, const float* alpha, int32_t seq_len, void* out,
+                             hipStream_t stream);
+
+/* Host-only: stable permutation that makes retrieval heads contiguous.
+ * mask[h] != 0 marks KV head h as a retrieval head. perm_out[i] receives the
+ * original KV head placed at position i (retrieval heads ascending, then
+ * streaming heads ascending); *n_retrieval_out the number of retrieval
+ * heads. */
+duo_status duo_head_permutation(const uint8_t* mask, int32_t n_kv_heads, int32_t* perm_out,
+                                int32_t* n_retrieval_out);
+
+/* Host-only: ring slot of token position p (the rule stated above), or -1
+ * for invalid arguments. */
+int32_t duo_ring_slot(int64_t position, int32_t sink, int32_t recent);
+
+/* Static text for a status code. */
+const char* duo_status_string(duo_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DUO_H_ */

@@ -1,0 +1,192 @@
+"""Python binding of the C ABI: torch tensors provide device memory and
+streams, the library does all the work.
+
+``DuoLayer`` owns (as torch uint8 tensors) the retrieval cache, the streaming
+ring and the workspace of one attention layer and forwards append / prefill /
+decode calls to libduo.so. ``mixed_forward`` is the stateless gate-blended
+forward. ``head_permutation`` and ``ring_slot`` are the host helpers.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_uint8, c_void_p
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import lib, check, make_desc, layout
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _check_act(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_TORCH = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+class DuoLayer:
+    """One attention layer with a full cache for retrieval KV heads [0, Hr)
+    and a sink + recent ring for streaming KV heads [Hr, Hkv)."""
+
+    def __init__(self, *, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 n_retrieval_kv_heads: int, capacity: int, softmax_scale: float,
+                 sink: int = 16, recent: int = 64, batch: int = 1, kv_dtype: str = "bf16",
+                 retrieval_dtype: Optional[str] = None, device="cuda",
+                 n_tokens_existing: int = 0):
+        self.desc = make_desc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                              head_dim=head_dim, n_retrieval_kv_heads=n_retrieval_kv_heads,
+                              sink=sink, recent=recent, capacity=capacity, kv_dtype=kv_dtype,
+                              retrieval_dtype=retrieval_dtype, softmax_scale=softmax_scale)
+        self.layout = layout(self.desc)
+        self.device = torch.device(device)
+        self.B, self.Hq, self.Hkv, self.D = batch, n_q_heads, n_kv_heads, head_dim
+        self.Hr, self.Hs = n_retrieval_kv_heads, n_kv_heads - n_retrieval_kv_heads
+        self.G = n_q_heads // n_kv_heads
+        self.S, self.R, self.capacity = sink, recent, capacity
+        self.kv_dtype = kv_dtype
+        self.retrieval_dtype = kv_dtype if retrieval_dtype is None else retrieval_dtype
+        lay = self.layout
+        self.rbuf = torch.zeros(max(lay.retrieval_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.sbuf = torch.zeros(max(lay.streaming_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.ws = torch.zeros(max(lay.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
+        h = c_void_p()
+        check(lib.duo_layer_init(byref(h), byref(self.desc), _ptr(self.rbuf), _ptr(self.sbuf),
+                                 _ptr(self.ws), n_tokens_existing, _stream_ptr(self.device)),
+              "duo_layer_init")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib.duo_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def n_tokens(self) -> int:
+        return int(lib.duo_layer_tokens(self._h))
+
+    # -- calls -----------------------------------------------------------------
+    def append_kv(self, k: torch.Tensor, v: torch.Tensor):
+        T = k.shape[1]
+        kvt = _TORCH[self.kv_dtype]
+        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt)
+        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt)
+        check(lib.duo_append_kv(self._h, _ptr(k), _ptr(v), T, _stream_ptr(self.device)),
+              "duo_append_kv")
+
+    def prefill_chunk(self, q, k, v, out=None):
+        T = q.shape[1]
+        kvt = _TORCH[self.kv_dtype]
+        _check_act(q, "q", (self.B, T, self.Hq, self.D), torch.bfloat16)
+        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt)
+        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt)
+        if out is None:
+            out = torch.empty_like(q)
+        _check_act(out, "out", (self.B, T, self.Hq, self.D), torch.bfloat16)
+        check(lib.duo_prefill_chunk(self._h, _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
+                                    _stream_ptr(self.device)), "duo_prefill_chunk")
+        return out
+
+    def decode(self, q, k, v, out=None):
+        kvt = _TORCH[self.kv_dtype]
+        _check_act(q, "q", (self.B, 1, self.Hq, self.D), torch.bfloat16)
+        _check_act(k, "k", (self.B, 1, self.Hkv, self.D), kvt)
+        _check_act(v, "v", (self.B, 1, self.Hkv, self.D), kvt)
+        if out is None:
+            out = torch.empty_like(q)
+        _check_act(out, "out", (self.B, 1, self.Hq, self.D), torch.bfloat16)
+        check(lib.duo_decode(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                             _stream_ptr(self.device)), "duo_decode")
+        return out
+
+    # -- views of the caller-owned caches (documented layout) -------------------
+    def retrieval_kv(self):
+        """(K, V) views [B, Hr, cap, D] of a bf16/fp16 retrieval cache."""
+        assert self.retrieval_dtype != "int4"
+        dt = _TORCH[self.kv_dtype]
+        shape = (self.B, self.Hr, self.capacity, self.D)
+        return (_bytes_view(self.rbuf, self.layout.k_offset, shape, dt),
+                _bytes_view(self.rbuf, self.layout.v_offset, shape, dt))
+
+    def retrieval_int4(self):
+        """(K codes, V codes [B,Hr,cap,D/2] u8, K sz, V sz [B,Hr,cap,D/32,2] fp16)."""
+        assert self.retrieval_dtype == "int4"
+        cs = (self.B, self.Hr, self.capacity, self.D // 2)
+        ss = (self.B, self.Hr, self.capacity, self.D // 32, 2)
+        return (_bytes_view(self.rbuf, self.layout.k_offset, cs, torch.uint8),
+                _bytes_view(self.rbuf, self.layout.v_offset, cs, torch.uint8),
+                _bytes_view(self.rbuf, self.layout.k_sz_offset, ss, torch.float16),
+                _bytes_view(self.rbuf, self.layout.v_sz_offset, ss, torch.float16))
+
+    def ring_kv(self):
+        """(K, V) views [B, Hs, S+R, D] of the streaming ring."""
+        dt = _TORCH[self.kv_dtype]
+        shape = (self.B, self.Hs, self.S + self.R, self.D)
+        return (_bytes_view(self.sbuf, self.layout.ring_k_offset, shape, dt),
+                _bytes_view(self.sbuf, self.layout.ring_v_offset, shape, dt))
+
+
+def _bytes_view(buf: torch.Tensor, offset: int, shape, dtype) -> torch.Tensor:
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return buf[offset:offset + nbytes].view(dtype).view(*shape)
+
+
+def mixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, *,
+                  softmax_scale: float, sink: int = 16, recent: int = 64, out=None):
+    """out_h = alpha[h // G] * full_h + (1 - alpha[h // G]) * streaming_h.
+    q [B,T,Hq,D] bf16, k/v [B,T,Hkv,D] bf16, alpha [Hkv] fp32 (device)."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16)
+    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16)
+    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16)
+    _check_act(alpha, "alpha", (Hkv,), torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_act(out, "out", (B, T, Hq, D), torch.bfloat16)
+    desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
+                     sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
+    check(lib.duo_mixed_forward(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), T,
+                                _ptr(out), _stream_ptr(q.device)), "duo_mixed_forward")
+    return out
+
+
+def head_permutation(mask: Sequence[int]):
+    """Stable permutation making retrieval KV heads contiguous (host call).
+    Returns (perm, n_retrieval): perm[i] = original KV head at position i."""
+    n = len(mask)
+    m = (c_uint8 * n)(*[1 if x else 0 for x in mask])
+    perm = (c_int32 * n)()
+    nr = c_int32()
+    check(lib.duo_head_permutation(m, n, perm, byref(nr)), "duo_head_permutation")
+    return list(perm), int(nr.value)
+
+
+def ring_slot(position: int, sink: int, recent: int) -> int:
+    return int(lib.duo_ring_slot(position, sink, recent))

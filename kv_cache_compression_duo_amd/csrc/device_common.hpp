@@ -1,0 +1,100 @@
+// Device helpers shared by the gfx950 kernels: 16-byte vector loads, bf16 /
+// fp16 <-> fp32 conversion, DPP lane reductions inside a row of 16 lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+// Streamed (read-once) 16-byte load: one global_load_dwordx4 with the
+// non-temporal hint, so that the KV sweep does not evict data that is reused.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  v4u32 r = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+  return u32x4{r.x, r.y, r.z, r.w};
+}
+
+// ---- element types ---------------------------------------------------------
+struct Bf16Tag {};
+struct Fp16Tag {};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  return (float)h;
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  return (float)h;
+}
+
+template <typename Tag>
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f);
+
+template <>
+__device__ __forceinline__ void unpack8<Bf16Tag>(const u32x4& v, float* f) {
+  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
+  f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z);
+  f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack8<Fp16Tag>(const u32x4& v, float* f) {
+  f[0] = f16lo(v.x); f[1] = f16hi(v.x);
+  f[2] = f16lo(v.y); f[3] = f16hi(v.y);
+  f[4] = f16lo(v.z); f[5] = f16hi(v.z);
+  f[6] = f16lo(v.w); f[7] = f16hi(v.w);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f2bf(a) | (f2bf(b) << 16);
+}
+
+// ---- DPP reductions --------------------------------------------------------
+// dpp_ctrl values (GCN/CDNA DPP): quad_perm [1,0,3,2] = 0xB1, quad_perm
+// [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16); every lane of the
+// group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) v += dpp<0xB1>(v);
+  if constexpr (N >= 4) v += dpp<0x4E>(v);
+  if constexpr (N >= 8) v += dpp<0x141>(v);
+  if constexpr (N >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
+// Butterfly across lane groups with xor distances >= 16 (ds_bpermute).
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace duo

@@ -1,0 +1,249 @@
+// C-ABI front end: argument validation, buffer layout, host token counter and
+// dispatch to the kernel launchers. Every check runs before any HIP call, so
+// a failed call enqueues nothing and leaves the layer unchanged.
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "duo_internal.hpp"
+
+namespace duo {
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int max_split_for(const duo_layer_desc& d) {
+  int64_t cap = d.retrieval_capacity;
+  int64_t s = (cap + kMinSplitTokens - 1) / kMinSplitTokens + 1;
+  return (int)(s < 1 ? 1 : s);
+}
+
+size_t ws_bytes(const duo_layer_desc& d, int max_split) {
+  size_t Hr = (size_t)d.n_retrieval_kv_heads, B = (size_t)d.batch;
+  size_t G = (size_t)(d.n_q_heads / d.n_kv_heads);
+  size_t cnt = align_up(B * Hr * sizeof(uint32_t) + 4, 256);
+  size_t ml = align_up(B * Hr * G * (size_t)max_split * 2 * sizeof(float), 256);
+  size_t acc = align_up(B * Hr * G * (size_t)max_split * (size_t)d.head_dim * sizeof(float), 256);
+  return cnt + ml + acc;
+}
+
+WsView ws_view(const duo_layer* L) {
+  const duo_layer_desc& d = L->d;
+  size_t Hr = (size_t)L->Hr, B = (size_t)d.batch, G = (size_t)L->G;
+  size_t cnt = align_up(B * Hr * sizeof(uint32_t) + 4, 256);
+  size_t ml = align_up(B * Hr * G * (size_t)L->max_split * 2 * sizeof(float), 256);
+  WsView v;
+  v.counters = reinterpret_cast<uint32_t*>(L->ws);
+  v.ml = reinterpret_cast<float*>(L->ws + cnt);
+  v.acc = reinterpret_cast<float*>(L->ws + cnt + ml);
+  return v;
+}
+
+static duo_status check_desc(const duo_layer_desc* d) {
+  if (!d) return DUO_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return DUO_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads) return DUO_ERR_INVALID_ARG;
+  int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return DUO_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return DUO_ERR_UNSUPPORTED;
+  if (d->n_retrieval_kv_heads < 0 || d->n_retrieval_kv_heads > d->n_kv_heads)
+    return DUO_ERR_INVALID_ARG;
+  if (d->sink < 0 || d->recent < 1) return DUO_ERR_INVALID_ARG;
+  if ((int64_t)d->sink + d->recent > 1024) return DUO_ERR_UNSUPPORTED;
+  if (d->retrieval_capacity < 0 || d->retrieval_capacity > (int64_t)INT32_MAX)
+    return DUO_ERR_INVALID_ARG;
+  if (d->kv_dtype != DUO_BF16 && d->kv_dtype != DUO_FP16) return DUO_ERR_UNSUPPORTED;
+  if (d->retrieval_dtype != d->kv_dtype && d->retrieval_dtype != DUO_INT4_G32)
+    return DUO_ERR_UNSUPPORTED;
+  if (!isfinite(d->softmax_scale)) return DUO_ERR_INVALID_ARG;
+  return DUO_OK;
+}
+
+}  // namespace duo
+
+using namespace duo;
+
+extern "C" {
+
+duo_status duo_layer_layout(const duo_layer_desc* d, duo_layout* out) {
+  duo_status st = check_desc(d);
+  if (st != DUO_OK) return st;
+  if (!out) return DUO_ERR_INVALID_ARG;
+  size_t B = (size_t)d->batch, D = (size_t)d->head_dim, cap = (size_t)d->retrieval_capacity;
+  size_t Hr = (size_t)d->n_retrieval_kv_heads, Hs = (size_t)(d->n_kv_heads - d->n_retrieval_kv_heads);
+  size_t W = (size_t)(d->sink + d->recent);
+  duo_layout L;
+  memset(&L, 0, sizeof(L));
+  if (d->retrieval_dtype == DUO_INT4_G32) {
+    size_t codes = align_up(B * Hr * cap * (D / 2), 256);
+    size_t sz = align_up(B * Hr * cap * (D / 32) * 2 * 2, 256);
+    L.k_offset = 0;
+    L.v_offset = codes;
+    L.k_sz_offset = 2 * codes;
+    L.v_sz_offset = 2 * codes + sz;
+    L.retrieval_bytes = 2 * codes + 2 * sz;
+  } else {
+    size_t arr = align_up(B * Hr * cap * D * 2, 256);
+    L.k_offset = 0;
+    L.v_offset = arr;
+    L.k_sz_offset = L.v_sz_offset = 0;
+    L.retrieval_bytes = 2 * arr;
+  }
+  size_t ring = align_up(B * Hs * W * D * 2, 256);
+  L.ring_k_offset = 0;
+  L.ring_v_offset = ring;
+  L.streaming_bytes = 2 * ring;
+  L.workspace_bytes = ws_bytes(*d, max_split_for(*d));
+  *out = L;
+  return DUO_OK;
+}
+
+duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrieval_buf,
+                          void* streaming_buf, void* workspace, int64_t n_tokens_existing,
+                          hipStream_t stream) {
+  if (!out) return DUO_ERR_INVALID_ARG;
+  duo_layout lay;
+  duo_status st = duo_layer_layout(d, &lay);
+  if (st != DUO_OK) return st;
+  if (n_tokens_existing < 0) return DUO_ERR_INVALID_ARG;
+  if (d->n_retrieval_kv_heads > 0 && n_tokens_existing > d->retrieval_capacity)
+    return DUO_ERR_CAPACITY;
+  if (lay.retrieval_bytes && !retrieval_buf) return DUO_ERR_INVALID_ARG;
+  if (lay.streaming_bytes && !streaming_buf) return DUO_ERR_INVALID_ARG;
+  if (!workspace) return DUO_ERR_INVALID_ARG;
+  if (!aligned(retrieval_buf, 256) || !aligned(streaming_buf, 256) || !aligned(workspace, 256))
+    return DUO_ERR_LAYOUT;
+  duo_layer* L = new (std::nothrow) duo_layer;
+  if (!L) return DUO_ERR_INVALID_ARG;
+  L->d = *d;
+  L->lay = lay;
+  L->rbuf = static_cast<char*>(retrieval_buf);
+  L->sbuf = static_cast<char*>(streaming_buf);
+  L->ws = static_cast<char*>(workspace);
+  L->n = n_tokens_existing;
+  L->G = d->n_q_heads / d->n_kv_heads;
+  L->Hr = d->n_retrieval_kv_heads;
+  L->Hs = d->n_kv_heads - d->n_retrieval_kv_heads;
+  L->max_split = max_split_for(*d);
+  if (launch_zero(workspace, lay.workspace_bytes, stream) != hipSuccess) {
+    delete L;
+    return DUO_ERR_HIP;
+  }
+  *out = L;
+  return DUO_OK;
+}
+
+duo_status duo_layer_destroy(duo_layer* L) {
+  delete L;
+  return DUO_OK;
+}
+
+int64_t duo_layer_tokens(const duo_layer* L) { return L ? L->n : -1; }
+
+static duo_status check_act(const void* p) {
+  if (!p) return DUO_ERR_INVALID_ARG;
+  if (!aligned(p, 16)) return DUO_ERR_LAYOUT;
+  return DUO_OK;
+}
+
+duo_status duo_append_kv(duo_layer* L, const void* k, const void* v, int32_t T,
+                         hipStream_t stream) {
+  if (!L || T < 1) return DUO_ERR_INVALID_ARG;
+  duo_status st;
+  if ((st = check_act(k)) != DUO_OK || (st = check_act(v)) != DUO_OK) return st;
+  if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
+  if (L->Hr > 0 && launch_append_cache(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
+  if (L->Hs > 0 && launch_append_ring(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
+  L->n += T;
+  return DUO_OK;
+}
+
+duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const void* v,
+                             int32_t T, void* out, hipStream_t stream) {
+  if (!L || T < 1) return DUO_ERR_INVALID_ARG;
+  duo_status st;
+  if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
+      (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
+    return st;
+  if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
+  if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
+  // Retrieval heads: append the chunk, then attend causally over the cache.
+  if (L->Hr > 0) {
+    if (launch_append_cache(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
+    if (launch_prefill_retrieval(L, q, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
+  }
+  // Streaming heads: attend over the ring as it was before the chunk plus the
+  // chunk, then update the ring (the chunk overwrites slots still being read).
+  if (L->Hs > 0) {
+    if (launch_prefill_streaming(L, q, k, v, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
+    if (launch_append_ring(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
+  }
+  L->n += T;
+  return DUO_OK;
+}
+
+duo_status duo_decode(duo_layer* L, const void* q, const void* k_new, const void* v_new,
+                      void* out, hipStream_t stream) {
+  if (!L) return DUO_ERR_INVALID_ARG;
+  duo_status st;
+  if ((st = check_act(q)) != DUO_OK || (st = check_act(k_new)) != DUO_OK ||
+      (st = check_act(v_new)) != DUO_OK || (st = check_act(out)) != DUO_OK)
+    return st;
+  if (L->Hr > 0 && L->n + 1 > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
+  if (L->n + 1 > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
+  hipError_t e;
+  if (L->d.retrieval_dtype == DUO_INT4_G32 && L->Hr > 0)
+    e = launch_decode_int4(L, q, k_new, v_new, out, stream);
+  else
+    e = launch_decode(L, q, k_new, v_new, out, stream);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  L->n += 1;
+  return DUO_OK;
+}
+
+duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void* k,
+                             const void* v, const float* alpha, int32_t T, void* out,
+                             hipStream_t stream) {
+  duo_status st = check_desc(d);
+  if (st != DUO_OK) return st;
+  if (d->kv_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (T < 1) return DUO_ERR_INVALID_ARG;
+  if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
+      (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
+    return st;
+  if (!alpha) return DUO_ERR_INVALID_ARG;
+  if (!aligned(alpha, 4)) return DUO_ERR_LAYOUT;
+  if (launch_mixed(*d, q, k, v, alpha, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+duo_status duo_head_permutation(const uint8_t* mask, int32_t n, int32_t* perm,
+                                int32_t* n_retrieval) {
+  if (!mask || !perm || !n_retrieval || n < 1) return DUO_ERR_INVALID_ARG;
+  int32_t w = 0;
+  for (int32_t h = 0; h < n; ++h)
+    if (mask[h]) perm[w++] = h;
+  *n_retrieval = w;
+  for (int32_t h = 0; h < n; ++h)
+    if (!mask[h]) perm[w++] = h;
+  return DUO_OK;
+}
+
+int32_t duo_ring_slot(int64_t p, int32_t sink, int32_t recent) {
+  if (p < 0 || sink < 0 || recent < 1) return -1;
+  if (p < sink) return (int32_t)p;
+  return (int32_t)(sink + (p - sink) % recent);
+}
+
+const char* duo_status_string(duo_status s) {
+  switch (s) {
+    case DUO_OK: return "ok";
+    case DUO_ERR_INVALID_ARG: return "invalid argument";
+    case DUO_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DUO_ERR_LAYOUT: return "bad layout or alignment";
+    case DUO_ERR_CAPACITY: return "retrieval cache capacity exceeded";
+    case DUO_ERR_HIP: return "HIP launch or API error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

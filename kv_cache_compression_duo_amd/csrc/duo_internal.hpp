@@ -1,0 +1,53 @@
+// Internal declarations shared by the C-ABI front end and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/duo.h"
+
+struct duo_layer {
+  duo_layer_desc d;
+  duo_layout lay;
+  char* rbuf;
+  char* sbuf;
+  char* ws;
+  int64_t n;      // tokens cached
+  int G, Hr, Hs;  // group size, retrieval / streaming KV heads
+  int max_split;  // split-K partial slots per retrieval (batch, KV head)
+};
+
+namespace duo {
+
+// Workspace layout: [counters: B*Hr u32, padded to 256 B][m,l: B*Hr*G*max_split*2 f32]
+//                   [acc: B*Hr*G*max_split*D f32]
+constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsView {
+  uint32_t* counters;
+  float* ml;
+  float* acc;
+};
+WsView ws_view(const duo_layer* L);
+size_t ws_bytes(const duo_layer_desc& d, int max_split);
+int max_split_for(const duo_layer_desc& d);
+
+// ---- launchers (return hipSuccess or the launch error) ----------------------
+hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v, int T,
+                               hipStream_t s);
+hipError_t launch_append_ring(const duo_layer* L, const void* k, const void* v, int T,
+                              hipStream_t s);
+hipError_t launch_decode(const duo_layer* L, const void* q, const void* k_new,
+                         const void* v_new, void* out, hipStream_t s);
+hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_new,
+                              const void* v_new, void* out, hipStream_t s);
+hipError_t launch_prefill_retrieval(const duo_layer* L, const void* q, int T, void* out,
+                                    hipStream_t s);
+hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const void* k,
+                                    const void* v, int T, void* out, hipStream_t s);
+hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, const void* v,
+                        const float* alpha, int T, void* out, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace duo

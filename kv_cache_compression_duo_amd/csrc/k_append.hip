@@ -1,0 +1,198 @@
+// Cache-append kernels: retrieval rows (verbatim or 4-bit group encoded), ring
+// slots of the streaming heads, and a zero-fill used for the workspace.
+//
+// The two caches per layer and the split of new K/V along the head axis follow
+// the xllm-io review "DuoAttention: Efficient Long-Context LLM Inference with
+// Retrieval and Streaming Heads", section 三 推理流程. The 4-bit encoding is
+// this library's reading of the 4-bit KV cache the same page names in section
+// 五 量化组合: per token, head and 32-channel group, fp16 scale
+// s = (max - min) / 15 and fp16 zero-point z = min, codes
+// rint((x - z) / s) clamped to [0, 15] (0 when s == 0), all in fp32 with IEEE
+// division so that the codes are reproducible bit for bit.
+#include "device_common.hpp"
+#include "duo_internal.hpp"
+
+namespace duo {
+
+// ---- verbatim retrieval rows -------------------------------------------------
+// One thread per 16-byte chunk: k/v [B][T][Hkv][D] -> cache [B][Hr][cap][D].
+__global__ void append_rows_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                   u32x4* __restrict__ kc, u32x4* __restrict__ vc, int B, int T,
+                                   int Hkv, int Hr, int chunks, int64_t cap, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)B * T * Hr * chunks;
+  if (i >= total) return;
+  int c = (int)(i % chunks);
+  int64_t r = i / chunks;
+  int h = (int)(r % Hr);
+  r /= Hr;
+  int t = (int)(r % T);
+  int b = (int)(r / T);
+  int64_t src = (((int64_t)b * T + t) * Hkv + h) * chunks + c;
+  int64_t dst = (((int64_t)b * Hr + h) * cap + n + t) * chunks + c;
+  kc[dst] = k[src];
+  vc[dst] = v[src];
+}
+
+// ---- 4-bit group encoding --------------------------------------------------
+template <typename Tag>
+__device__ __forceinline__ void encode_group_part(const u32x4& raw, uint32_t* codes_out,
+                                                  uint32_t* sz_out) {
+  // Four consecutive lanes hold one 32-channel group, 8 channels each.
+  float x[8];
+  unpack8<Tag>(raw, x);
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    mn = fminf(mn, x[j]);
+    mx = fmaxf(mx, x[j]);
+  }
+  // min / max over the 4 lanes of the group (quad_perm butterflies)
+  mn = fminf(mn, dpp<0xB1>(mn));
+  mx = fmaxf(mx, dpp<0xB1>(mx));
+  mn = fminf(mn, dpp<0x4E>(mn));
+  mx = fmaxf(mx, dpp<0x4E>(mx));
+  _Float16 s16 = (_Float16)__fdiv_rn(mx - mn, 15.0f);
+  _Float16 z16 = (_Float16)mn;
+  float s = (float)s16, z = (float)z16;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float c = 0.0f;
+    if (s != 0.0f) {
+      c = rintf(__fdiv_rn(x[j] - z, s));
+      c = fminf(fmaxf(c, 0.0f), 15.0f);
+    }
+    packed |= ((uint32_t)c & 0xFu) << (4 * j);
+  }
+  *codes_out = packed;
+  *sz_out = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+}
+
+// One thread per 8 channels; the thread count per (b,t,h) row is D/8, a
+// multiple of 4, so the 4 lanes of a group are always in one quad.
+template <typename Tag>
+__global__ void append_int4_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                   uint32_t* __restrict__ kcodes, uint32_t* __restrict__ vcodes,
+                                   uint32_t* __restrict__ ksz, uint32_t* __restrict__ vsz, int B,
+                                   int T, int Hkv, int Hr, int chunks, int64_t cap, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)B * T * Hr * chunks;
+  // Every lane of a quad is either in range or not (total is a multiple of 4),
+  // so the DPP exchanges below never read an inactive lane.
+  if (i >= total) return;
+  int c = (int)(i % chunks);
+  int64_t r = i / chunks;
+  int h = (int)(r % Hr);
+  r /= Hr;
+  int t = (int)(r % T);
+  int b = (int)(r / T);
+  int64_t src = (((int64_t)b * T + t) * Hkv + h) * chunks + c;
+  int64_t row = ((int64_t)b * Hr + h) * cap + n + t;
+  uint32_t kq, ks, vq, vs;
+  encode_group_part<Tag>(k[src], &kq, &ks);
+  encode_group_part<Tag>(v[src], &vq, &vs);
+  kcodes[row * chunks + c] = kq;  // 8 nibbles = 4 bytes per thread
+  vcodes[row * chunks + c] = vq;
+  if ((c & 3) == 0) {
+    int groups = chunks / 4;
+    ksz[row * groups + c / 4] = ks;
+    vsz[row * groups + c / 4] = vs;
+  }
+}
+
+// ---- ring slots --------------------------------------------------------------
+// Writes the positions of [n, n+T) that survive the chunk: those < S and the
+// last R positions >= S. They land in distinct slots, so threads never collide.
+__global__ void append_ring_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                   u32x4* __restrict__ kr, u32x4* __restrict__ vr, int B, int T,
+                                   int Hkv, int Hr, int Hs, int chunks, int S, int R, int64_t n,
+                                   int cnt_sink, int64_t lo_recent, int cnt_recent) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int cnt = cnt_sink + cnt_recent;
+  int64_t total = (int64_t)B * cnt * Hs * chunks;
+  if (i >= total) return;
+  int c = (int)(i % chunks);
+  int64_t r = i / chunks;
+  int hs = (int)(r % Hs);
+  r /= Hs;
+  int e = (int)(r % cnt);
+  int b = (int)(r / cnt);
+  int64_t p = e < cnt_sink ? n + e : lo_recent + (e - cnt_sink);
+  int slot = p < S ? (int)p : S + (int)((p - S) % R);
+  int t = (int)(p - n);
+  int64_t src = (((int64_t)b * T + t) * Hkv + Hr + hs) * chunks + c;
+  int64_t dst = (((int64_t)b * Hs + hs) * (S + R) + slot) * chunks + c;
+  kr[dst] = k[src];
+  vr[dst] = v[src];
+}
+
+__global__ void zero_kernel(u32x4* p, int64_t n16) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+static inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  zero_kernel<<<blocks_for(n16, 256), 256, 0, s>>>(static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v, int T,
+                               hipStream_t s) {
+  const duo_layer_desc& d = L->d;
+  int chunks = d.head_dim / 8;
+  int64_t total = (int64_t)d.batch * T * L->Hr * chunks;
+  if (total == 0) return hipSuccess;
+  unsigned grid = blocks_for(total, 256);
+  if (d.retrieval_dtype == DUO_INT4_G32) {
+    auto* kq = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.k_offset);
+    auto* vq = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.v_offset);
+    auto* ks = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.k_sz_offset);
+    auto* vs = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.v_sz_offset);
+    if (d.kv_dtype == DUO_FP16)
+      append_int4_kernel<Fp16Tag><<<grid, 256, 0, s>>>(
+          static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), kq, vq, ks, vs, d.batch, T,
+          d.n_kv_heads, L->Hr, chunks, d.retrieval_capacity, L->n);
+    else
+      append_int4_kernel<Bf16Tag><<<grid, 256, 0, s>>>(
+          static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), kq, vq, ks, vs, d.batch, T,
+          d.n_kv_heads, L->Hr, chunks, d.retrieval_capacity, L->n);
+  } else {
+    append_rows_kernel<<<grid, 256, 0, s>>>(
+        static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+        reinterpret_cast<u32x4*>(L->rbuf + L->lay.k_offset),
+        reinterpret_cast<u32x4*>(L->rbuf + L->lay.v_offset), d.batch, T, d.n_kv_heads, L->Hr,
+        chunks, d.retrieval_capacity, L->n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_ring(const duo_layer* L, const void* k, const void* v, int T,
+                              hipStream_t s) {
+  const duo_layer_desc& d = L->d;
+  const int64_t n = L->n, S = d.sink, R = d.recent;
+  // sinks among the chunk: positions [n, min(S, n+T))
+  int64_t sink_hi = n + T < S ? n + T : S;
+  int cnt_sink = sink_hi > n ? (int)(sink_hi - n) : 0;
+  // last R positions at or after S: [max(S, n, n+T-R), n+T)
+  int64_t lo = n + T - R;
+  if (lo < S) lo = S;
+  if (lo < n) lo = n;
+  int cnt_recent = n + T > lo ? (int)(n + T - lo) : 0;
+  int chunks = d.head_dim / 8;
+  int64_t total = (int64_t)d.batch * (cnt_sink + cnt_recent) * L->Hs * chunks;
+  if (total == 0) return hipSuccess;
+  append_ring_kernel<<<blocks_for(total, 256), 256, 0, s>>>(
+      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+      reinterpret_cast<u32x4*>(L->sbuf + L->lay.ring_k_offset),
+      reinterpret_cast<u32x4*>(L->sbuf + L->lay.ring_v_offset), d.batch, T, d.n_kv_heads, L->Hr,
+      L->Hs, chunks, d.sink, d.recent, n, cnt_sink, lo, cnt_recent);
+  return hipGetLastError();
+}
+
+}  // namespace duo

@@ -1,0 +1,83 @@
+"""Helpers for the GPU parity tests: device checks, head routing through the
+C ABI, and the comparison at the tolerance the parity bar states
+(max |o_gpu - o_ref| <= 2e-2 and ||o_gpu - o_ref|| / ||o_ref|| <= 5e-3,
+in float64, separately over the retrieval and the streaming heads)."""
+import sys
+
+import numpy as np
+import torch
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU")
+    import kv_cache_compression_duo_amd as duo  # fails loudly without libduo.so
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, dtype=torch.bfloat16, dev="cuda:0"):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype).to(dev)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), "non-finite GPU output"
+    d = got - ref
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)) if d.size else 0.0
+    return max_abs, rel
+
+
+def assert_close(got, ref, label, max_abs=MAX_ABS, rel_l2=REL_L2):
+    ma, rl = errors(got, ref)
+    say(f"  {label}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    assert ma <= max_abs and rl <= rel_l2, f"{label}: max_abs={ma:.3e} rel_l2={rl:.3e}"
+
+
+def assert_blocks_close(got, ref, retrieval_q_heads, label, head_axis=-2):
+    """Compare the retrieval-head and streaming-head blocks separately.
+    ``retrieval_q_heads`` is a boolean per query head (original order)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rmask = np.asarray(retrieval_q_heads, bool)
+    if rmask.any():
+        assert_close(np.take(got, np.where(rmask)[0], axis=head_axis),
+                     np.take(ref, np.where(rmask)[0], axis=head_axis), label + " retrieval")
+    if (~rmask).any():
+        assert_close(np.take(got, np.where(~rmask)[0], axis=head_axis),
+                     np.take(ref, np.where(~rmask)[0], axis=head_axis), label + " streaming")
+
+
+class Routed:
+    """Reorder heads with the library's permutation (retrieval first) on the way
+    in and restore the caller's order on the way out."""
+
+    def __init__(self, mask, G):
+        from kv_cache_compression_duo_amd import head_permutation
+        self.perm, self.nr = head_permutation(list(mask))
+        self.G = G
+        self.q_idx = torch.tensor([p * G + g for p in self.perm for g in range(G)])
+        inv = [0] * len(self.q_idx)
+        for i, p in enumerate(self.q_idx.tolist()):
+            inv[p] = i
+        self.q_inv = torch.tensor(inv)
+        self.kv_idx = torch.tensor(self.perm)
+
+    def q(self, t):   # [..., Hq, D] along dim -2
+        return t.index_select(-2, self.q_idx.to(t.device)).contiguous()
+
+    def kv(self, t):
+        return t.index_select(-2, self.kv_idx.to(t.device)).contiguous()
+
+    def out(self, t):
+        return t.index_select(-2, self.q_inv.to(t.device)).contiguous()

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+symbol include/duo.h declares, buffer layouts, argument validation before any
+HIP call, and the host helpers against the oracle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from duo_synth import rng
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from kv_cache_compression_duo_amd import _lib
+    return _lib
+
+
+def test_every_declared_symbol_is_exported():
+    text = open(os.path.join(ROOT, "include", "duo.h")).read()
+    names = set(re.findall(r"^[\w\s\*]*?\b(duo_\w+)\s*\(", text, flags=re.M))
+    assert {"duo_append_kv", "duo_prefill_chunk", "duo_decode", "duo_mixed_forward"} <= names
+    raw = ctypes.CDLL(_lib().LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def _desc(**kw):
+    base = dict(n_q_heads=32, n_kv_heads=8, head_dim=128, n_retrieval_kv_heads=4, capacity=1000,
+                softmax_scale=0.088)
+    base.update(kw)
+    return _lib().make_desc(**base)
+
+
+def test_layout_sizes():
+    L = _lib()
+    lay = L.layout(_desc())
+    assert lay.retrieval_bytes == 2 * 4 * 1000 * 128 * 2
+    assert lay.v_offset == 4 * 1000 * 128 * 2
+    assert lay.streaming_bytes == 2 * 4 * 80 * 128 * 2
+    lay4 = L.layout(_desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=1024))
+    codes = 4 * 1024 * 64
+    sz = 4 * 1024 * 4 * 2 * 2
+    assert lay4.v_offset == codes and lay4.k_sz_offset == 2 * codes
+    assert lay4.v_sz_offset == 2 * codes + sz
+    assert lay4.retrieval_bytes == 2 * codes + 2 * sz
+    # 160 bytes per token per retrieval head for D = 128
+    assert lay4.retrieval_bytes == 160 * 4 * 1024
+    for x in (lay, lay4):
+        for f in ("v_offset", "k_sz_offset", "v_sz_offset", "ring_v_offset"):
+            assert getattr(x, f) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2),
+    (dict(n_q_heads=30), 1),
+    (dict(n_q_heads=8 * 3), 2),          # group of 3
+    (dict(n_retrieval_kv_heads=9), 1),
+    (dict(recent=0), 1),
+    (dict(sink=-1), 1),
+    (dict(capacity=-5), 1),
+    (dict(kv_dtype="bf16", retrieval_dtype="fp16"), 2),
+    (dict(softmax_scale=float("inf")), 1),
+])
+def test_bad_descriptor_rejected(kw, status):
+    L = _lib()
+    out = L.Layout()
+    assert L.lib.duo_layer_layout(ctypes.byref(_desc(**kw)), ctypes.byref(out)) == status
+
+
+def test_init_validates_before_any_hip_call():
+    L = _lib()
+    h = ctypes.c_void_p()
+    d = _desc()
+    # null buffers
+    assert L.lib.duo_layer_init(ctypes.byref(h), ctypes.byref(d), None, None, None, 0, None) == 1
+    # misaligned buffers
+    assert L.lib.duo_layer_init(ctypes.byref(h), ctypes.byref(d), 0x1008, 0x2000, 0x3000, 0,
+                                None) == 3
+    # existing tokens beyond capacity
+    assert L.lib.duo_layer_init(ctypes.byref(h), ctypes.byref(d), 0x1000, 0x2000, 0x3000, 1001,
+                                None) == 4
+    assert L.lib.duo_layer_init(ctypes.byref(h), ctypes.byref(d), 0x1000, 0x2000, 0x3000, -1,
+                                None) == 1
+    assert h.value is None
+
+
+def test_calls_reject_null_layer():
+    L = _lib()
+    assert L.lib.duo_append_kv(None, 0x1000, 0x1000, 1, None) == 1
+    assert L.lib.duo_prefill_chunk(None, 0x1000, 0x1000, 0x1000, 1, 0x1000, None) == 1
+    assert L.lib.duo_decode(None, 0x1000, 0x1000, 0x1000, 0x1000, None) == 1
+    assert L.lib.duo_layer_tokens(None) == -1
+    assert L.lib.duo_layer_destroy(None) == 0
+
+
+def test_mixed_forward_validation():
+    L = _lib()
+    d = _desc()
+    f = L.lib.duo_mixed_forward
+    assert f(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, 0, 0x1000, None) == 1
+    assert f(ctypes.byref(d), 0x1008, 0x1000, 0x1000, 0x1000, 16, 0x1000, None) == 3
+    assert f(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 16, 0x1000, None) == 1
+    d16 = _desc(kv_dtype="fp16")
+    assert f(ctypes.byref(d16), 0x1000, 0x1000, 0x1000, 0x1000, 16, 0x1000, None) == 2
+
+
+def test_status_strings():
+    L = _lib()
+    assert L.status_string(0) == "ok"
+    assert "capacity" in L.status_string(4)
+
+
+def test_head_permutation_matches_oracle():
+    from kv_cache_compression_duo_amd import head_permutation
+    g = rng(51)
+    for _ in range(200):
+        H = int(g.integers(1, 65))
+        mask = [int(x) for x in g.integers(0, 2, size=H)]
+        assert head_permutation(mask) == oracle.head_permutation(mask)
+    assert head_permutation([1, 0, 0, 0, 0, 1, 0, 0]) == ([0, 5, 1, 2, 3, 4, 6, 7], 2)
+
+
+def test_ring_slot_matches_oracle():
+    from kv_cache_compression_duo_amd import ring_slot
+    for S, R in [(16, 64), (2, 3), (0, 1), (5, 7)]:
+        for p in range(0, 500):
+            assert ring_slot(p, S, R) == oracle.ring_slot(p, S, R)
+    assert ring_slot(-1, 16, 64) == -1
+    assert ring_slot(3, 16, 0) == -1

@@ -1,0 +1,223 @@
+"""GPU parity of context append + decode against the oracle (through the C ABI).
+
+Covers: the 8-head D=64 layer with retrieval heads {0,5}; the Llama-2-7B
+decode layer (32x128, 8 retrieval heads by seed) at a ragged context and at
+its full 32768-token context; GQA with an fp16 ring; ring boundaries around
+S and S+R; all-streaming and all-retrieval layers; batch 2; bit-exact cache
+and ring contents; a needle that only retrieval heads can see; determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from duo_synth import WORKLOADS, make_inputs, random_case, round_fp16, rng, normal
+from gpu_util import Routed, assert_blocks_close, assert_close, device, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_decode_case(inp, *, context, steps, kv_dtype="bf16", batch_rep=1, check_bytes=True,
+                     label=""):
+    """Fill the context with duo_append_kv, then decode ``steps`` tokens, each
+    compared with the oracle layer (original head order)."""
+    import kv_cache_compression_duo_amd as duo
+    w = inp.workload
+    dev = device()
+    Hq, Hkv, D = inp.q_steps.shape[1], w.n_kv_heads, w.head_dim
+    G = Hq // Hkv
+    mask = inp.retrieval_mask
+    r = Routed(mask, G)
+    tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float16
+    lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=r.nr,
+                       capacity=context + steps, softmax_scale=w.softmax_scale, sink=w.sink,
+                       recent=w.recent, batch=batch_rep, kv_dtype=kv_dtype, device=dev)
+    orc = oracle.OracleLayer(Hq, Hkv, D, mask, w.softmax_scale, w.sink, w.recent)
+    if context:
+        kc = r.kv(to_dev(inp.k[:context], tdt))[None].repeat(batch_rep, 1, 1, 1).contiguous()
+        vc = r.kv(to_dev(inp.v[:context], tdt))[None].repeat(batch_rep, 1, 1, 1).contiguous()
+        lay.append_kv(kc, vc)
+        orc.append(inp.k[:context], inp.v[:context])
+    assert lay.n_tokens == context
+    rq = np.repeat(np.array([mask[h // G] for h in range(Hq)], bool)[None], 1, 0)[0]
+    for s in range(steps):
+        q = r.q(to_dev(inp.q_steps[s]))[None, None].repeat(batch_rep, 1, 1, 1).contiguous()
+        k = r.kv(to_dev(inp.k_steps[s], tdt))[None, None].repeat(batch_rep, 1, 1, 1).contiguous()
+        v = r.kv(to_dev(inp.v_steps[s], tdt))[None, None].repeat(batch_rep, 1, 1, 1).contiguous()
+        out = lay.decode(q, k, v)
+        ref = orc.decode(inp.q_steps[s], inp.k_steps[s], inp.v_steps[s])
+        got = r.out(out).float().cpu().numpy()
+        for b in range(batch_rep):
+            assert_blocks_close(got[b, 0], ref, rq, f"{label} step {s} b{b}", head_axis=0)
+    assert lay.n_tokens == context + steps
+    if check_bytes:
+        torch.cuda.synchronize()
+        _check_cache_bytes(lay, orc, inp, r, context, steps, tdt)
+    return lay
+
+
+def _check_cache_bytes(lay, orc, inp, r, context, steps, tdt):
+    """Retrieval cache rows and ring slots equal the appended inputs bit for bit."""
+    n = context + steps
+    allk = np.concatenate([x for x in (inp.k[:context], inp.k_steps[:steps]) if x is not None])
+    allv = np.concatenate([x for x in (inp.v[:context], inp.v_steps[:steps]) if x is not None])
+    kdev = to_dev(allk, tdt).cpu()
+    vdev = to_dev(allv, tdt).cpu()
+    if lay.Hr:
+        K, V = lay.retrieval_kv()
+        for i in range(lay.Hr):
+            h = r.perm[i]
+            assert torch.equal(K[0, i, :n].cpu(), kdev[:, h]), f"retrieval K head {h}"
+            assert torch.equal(V[0, i, :n].cpu(), vdev[:, h]), f"retrieval V head {h}"
+    if lay.Hs:
+        K, V = lay.ring_kv()
+        for i in range(lay.Hs):
+            h = r.perm[lay.Hr + i]
+            held = orc.ring_contents(h)
+            assert held == oracle.ring_positions_after(n, lay.S, lay.R)
+            for slot, p in enumerate(held):
+                if p < 0:
+                    continue
+                assert torch.equal(K[0, i, slot].cpu(), kdev[p, h]), (h, slot, p)
+                assert torch.equal(V[0, i, slot].cpu(), vdev[p, h]), (h, slot, p)
+
+
+def test_decode_mha8_d64():
+    w = WORKLOADS["mha8_d64_seq1024"]
+    say(f"case: {w.key} append 1024 + 16 decode")
+    inp = make_inputs(w)
+    _run_decode_case(inp, context=1024, steps=16, label=w.key)
+
+
+def test_decode_llama2_ragged_context():
+    w = WORKLOADS["llama2_7b_decode_32k"]
+    say(f"case: {w.key} context 3001 + 5 decode")
+    inp = make_inputs(w, tokens=3001, steps=5)
+    _run_decode_case(inp, context=3001, steps=5, label=w.key)
+
+
+def test_decode_llama2_full_context():
+    w = WORKLOADS["llama2_7b_decode_32k"]
+    say(f"case: {w.key} context 32768 + 3 decode")
+    inp = make_inputs(w, steps=3)
+    _run_decode_case(inp, context=32768, steps=3, check_bytes=False, label=w.key)
+
+
+def test_decode_gqa_fp16_ring():
+    w = WORKLOADS["llama3_8b_int4_decode_1m"]
+    import dataclasses
+    w16 = dataclasses.replace(w, kv_dtype="fp16")   # fp16 retrieval cache, fp16 ring
+    say("case: GQA 32q/8kv fp16 KV, context 5000 + 4 decode")
+    inp = make_inputs(w16, tokens=5000, steps=4)
+    _run_decode_case(inp, context=5000, steps=4, kv_dtype="fp16", label="gqa-fp16")
+
+
+@pytest.mark.parametrize("context", [0, 1, 15, 16, 17, 79, 80, 81, 200, 256, 257])
+def test_decode_ring_boundaries(context):
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["mha8_d64_seq1024"], n_q_heads=4, n_kv_heads=2,
+                            fixed_retrieval=(0,), softmax_scale=0.125)
+    say(f"case: ring boundary context={context}")
+    inp = make_inputs(w, tokens=max(context, 1), steps=3, seed=2000 + context)
+    _run_decode_case(inp, context=context, steps=3, label=f"ctx{context}")
+
+
+@pytest.mark.parametrize("S,R", [(0, 1), (2, 3), (4, 100)])
+def test_decode_other_windows(S, R):
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["mha8_d64_seq1024"], n_q_heads=8, n_kv_heads=4,
+                            fixed_retrieval=(1, 2), sink=S, recent=R, head_dim=128)
+    say(f"case: window S={S} R={R}")
+    inp = make_inputs(w, tokens=300, steps=4, seed=3000 + S + R)
+    _run_decode_case(inp, context=300, steps=4, label=f"S{S}R{R}")
+
+
+@pytest.mark.parametrize("heads", [(), (0, 1, 2, 3)])
+def test_decode_all_streaming_or_all_retrieval(heads):
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["llama2_7b_decode_32k"], n_q_heads=8, n_kv_heads=4,
+                            fixed_retrieval=heads)
+    say(f"case: retrieval heads {heads}")
+    inp = make_inputs(w, tokens=700, steps=3, seed=4000 + len(heads))
+    _run_decode_case(inp, context=700, steps=3, label=f"hr{len(heads)}")
+
+
+def test_decode_batch2_and_group8():
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["llama3_8b_int4_decode_1m"], n_q_heads=16, n_kv_heads=2,
+                            kv_dtype="bf16", ring_dtype="bf16", fixed_retrieval=(1,))
+    say("case: batch 2, G=8")
+    inp = make_inputs(w, tokens=1500, steps=3, seed=5000)
+    _run_decode_case(inp, context=1500, steps=3, batch_rep=2, check_bytes=False, label="b2g8")
+
+
+def test_needle_routes_by_head_class():
+    """A key planted at position 500 with a logit ~60 above the rest: every
+    retrieval head returns ~v_needle, no streaming head does."""
+    import kv_cache_compression_duo_amd as duo
+    dev = device()
+    Hq = Hkv = 8
+    D, N = 64, 1000
+    mask = np.array([0, 1, 0, 0, 1, 0, 1, 0], np.uint8)
+    g = rng(77)
+    k = normal(g, (N + 1, Hkv, D)) * 0.5
+    v = normal(g, (N + 1, Hkv, D))
+    k[500, :, :] = 0.0
+    k[500, :, 0] = 60.0
+    q = np.zeros((Hq, D), np.float32)
+    q[:, 0] = 1.0
+    k = k.astype(np.float32)
+    v = v.astype(np.float32)
+    r = Routed(mask, 1)
+    lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=r.nr,
+                       capacity=N + 1, softmax_scale=1.0, device=dev)
+    lay.append_kv(r.kv(to_dev(k[:N]))[None], r.kv(to_dev(v[:N]))[None])
+    out = lay.decode(r.q(to_dev(q))[None, None], r.kv(to_dev(k[N]))[None, None],
+                     r.kv(to_dev(v[N]))[None, None])
+    got = r.out(out).float().cpu().numpy()[0, 0]
+    vn = torch.from_numpy(v[500]).to(torch.bfloat16).float().numpy()
+    for h in range(Hq):
+        err = np.abs(got[h] - vn[h]).max()
+        say(f"  head {h} ({'retrieval' if mask[h] else 'streaming'}): |o - v_needle| = {err:.3e}")
+        if mask[h]:
+            assert err < 2e-2
+        else:
+            assert err > 0.3
+
+
+def test_decode_is_deterministic():
+    w = WORKLOADS["llama2_7b_decode_32k"]
+    inp = make_inputs(w, tokens=2000, steps=2)
+    outs = []
+    import kv_cache_compression_duo_amd as duo
+    dev = device()
+    r = Routed(inp.retrieval_mask, 1)
+    for _ in range(2):
+        lay = duo.DuoLayer(n_q_heads=32, n_kv_heads=32, head_dim=128, n_retrieval_kv_heads=r.nr,
+                           capacity=2002, softmax_scale=1.0, device=dev)
+        lay.append_kv(r.kv(to_dev(inp.k))[None], r.kv(to_dev(inp.v))[None])
+        o = [lay.decode(r.q(to_dev(inp.q_steps[s]))[None, None],
+                        r.kv(to_dev(inp.k_steps[s]))[None, None],
+                        r.kv(to_dev(inp.v_steps[s]))[None, None]).cpu() for s in range(2)]
+        outs.append(torch.stack(o))
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_decode_capacity_error_leaves_state():
+    import kv_cache_compression_duo_amd as duo
+    dev = device()
+    lay = duo.DuoLayer(n_q_heads=4, n_kv_heads=2, head_dim=64, n_retrieval_kv_heads=1,
+                       capacity=3, softmax_scale=0.125, device=dev)
+    z = torch.zeros(1, 3, 2, 64, dtype=torch.bfloat16, device=dev)
+    lay.append_kv(z, z)
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros(1, 1, 2, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(duo.DuoError) as e:
+        lay.decode(q, kv, kv)
+    assert e.value.status == 4
+    assert lay.n_tokens == 3
+    with pytest.raises(duo.DuoError):
+        lay.append_kv(z[:, :1], z[:, :1])
+    assert lay.n_tokens == 3
