@@ -21,6 +21,7 @@ SOURCES = [
     "duo_api.cpp",
     "k_append.hip",
     "k_decode.hip",
+    "k_attn.hip",
     "k_stubs.hip",
 ]
 

@@ -164,6 +164,7 @@ duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const v
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
     return st;
+  if (L->d.kv_dtype != DUO_BF16 || L->d.retrieval_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
   // Retrieval heads: append the chunk, then attend causally over the cache.

@@ -1,0 +1,414 @@
+// Tiled softmax attention on bf16 MFMA for the prefill paths and the
+// gate-blended identification forward.
+//
+// What is computed (xllm-io review "DuoAttention: Efficient Long-Context LLM
+// Inference with Retrieval and Streaming Heads", section 三 核心公式):
+//   retrieval heads: softmax over keys j <= i (causal) of scale * q_i . k_j;
+//   streaming heads: the same under the Lambda mask, keys j <= i with
+//     j < sink or i - j < recent;
+//   mixed (identification) forward: alpha * full + (1 - alpha) * streaming
+//     with one alpha per KV head (same section, 混合注意力; paperlayer summary
+//     of arXiv 2410.10819v1, section 2).
+// Prefill is chunked: a chunk's retrieval heads attend over the full cache
+// (the chunk already appended), its streaming heads over the ring as it was
+// before the chunk plus the chunk itself, so activation memory scales with the
+// chunk (xllm-io review, section 三 预填充阶段; paperlayer summary, section 2
+// Chunked Pre-filling). The pages run this step with FlashAttention-2 on A100;
+// the kernel below is a gfx950 design of the same exact computation.
+//
+// gfx950 design:
+//   * a block is 4 waves; a wave owns 32 query rows (32 tokens of one query
+//     head). The HB heads of a block share one KV head (GQA grouping), so one
+//     K/V tile in LDS serves up to 4 query heads;
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16. In this
+//     orientation a lane holds one query's scores, so the softmax needs one
+//     cross-lane exchange per tile, and the score accumulator is directly the
+//     B operand of the PV product (keys permuted inside each 16-key slice,
+//     which a sum over keys does not see);
+//   * K tiles are stored row-major in LDS (rows padded by 16 bytes), V tiles
+//     transposed (d-major, 8-byte key chunks XOR-swizzled by d) so that both
+//     MFMA operands are read with ds_read_b128 / ds_read_b64;
+//   * the next tile's global loads are in flight while the current tile is
+//     computed; query tiles are launched longest-first (causal imbalance).
+#include "device_common.hpp"
+#include "duo_internal.hpp"
+
+namespace duo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum { MODE_RETRIEVAL = 0, MODE_STREAMING = 1, MODE_MIXED = 2 };
+
+struct AttnArgs {
+  const uint16_t* q;     // [B][T][Hq][D]
+  uint16_t* out;         // [B][T][Hq][D]
+  const uint16_t* k_in;  // chunk / sequence K, V [B][T][Hkv][D]
+  const uint16_t* v_in;
+  const uint16_t* kc;    // retrieval cache [B][Hr][cap][D]
+  const uint16_t* vc;
+  const uint16_t* kr;    // ring [B][Hs][S+R][D]
+  const uint16_t* vr;
+  const float* alpha;    // [Hkv] (mixed)
+  int T, Hq, Hkv, Hr, Hs, G, S, R;
+  int64_t cap;
+  int n;         // absolute position of token 0 of the chunk (0 for mixed)
+  int n_qtiles;  // query token tiles
+  int kv_base;   // first KV head handled by the launch
+  float scale_log2;
+};
+
+constexpr int kBN = 64;  // keys per tile
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int D>
+struct KeySrc {
+  // Base of key row `p` (absolute position) for the given mode. Positions no
+  // query of the launch may attend are mapped to some valid row (the mask
+  // removes them), so every address stays inside its buffer.
+  template <int MODE>
+  static __device__ __forceinline__ const uint16_t* row(const AttnArgs& a, int b, int kv, int p,
+                                                      bool v) {
+    if constexpr (MODE == MODE_RETRIEVAL) {
+      const int nk = a.n + a.T;
+      const int pc = p < nk ? (p < 0 ? 0 : p) : nk - 1;
+      const uint16_t* base = v ? a.vc : a.kc;
+      return base + (((int64_t)b * a.Hr + kv) * a.cap + pc) * D;
+    } else if constexpr (MODE == MODE_MIXED) {
+      const int pc = p < a.T ? (p < 0 ? 0 : p) : a.T - 1;
+      const uint16_t* base = v ? a.v_in : a.k_in;
+      return base + (((int64_t)b * a.T + pc) * a.Hkv + kv) * D;
+    } else {
+      const uint16_t* in = v ? a.v_in : a.k_in;
+      if (p >= a.n && p < a.n + a.T)
+        return in + (((int64_t)b * a.T + (p - a.n)) * a.Hkv + kv) * D;
+      const int rlo = a.n - a.R > a.S ? a.n - a.R : a.S;
+      if (p >= 0 && p < a.n && (p < a.S || p >= rlo)) {
+        const int slot = p < a.S ? p : a.S + (p - a.S) % a.R;
+        const uint16_t* ring = v ? a.vr : a.kr;
+        return ring + (((int64_t)b * a.Hs + (kv - a.Hr)) * (a.S + a.R) + slot) * D;
+      }
+      return in + ((int64_t)b * a.T * a.Hkv + kv) * D;  // masked for every query
+    }
+  }
+};
+
+template <int D, int HB, int MODE>
+__global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(AttnArgs a) {
+  constexpr int KS = D / 16;          // k-steps of the QK product
+  constexpr int DB = D / 32;          // 32-row d-blocks of the PV product
+  constexpr int TOKW = 32;            // tokens per wave
+  constexpr int BMT = TOKW * 4 / HB;  // tokens per block
+  constexpr int KPAD = D + 8;         // K tile row stride in LDS (elements)
+  constexpr int KLD = D / 32;         // 16-byte K loads per thread
+  constexpr bool kMixed = MODE == MODE_MIXED;
+  __shared__ __align__(16) uint16_t Ks[kBN * KPAD];
+  __shared__ __align__(16) uint16_t Vt[D * kBN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h2 = lane >> 5, q32 = lane & 31;
+  const int b = blockIdx.z;
+  const int groups = a.G / HB;
+  const int kv = a.kv_base + (int)blockIdx.y / groups;
+  const int head = kv * a.G + ((int)blockIdx.y % groups) * HB + (wave % HB);
+  const int tile = a.n_qtiles - 1 - (int)blockIdx.x;  // longest rows first
+  const int tok0 = tile * BMT;
+  const int t_q = tok0 + (wave / HB) * TOKW + q32;   // this lane's query token
+  const int t_qc = t_q < a.T ? t_q : a.T - 1;
+  const int i_q = a.n + t_q;                          // and its position
+  const int blk_last = (tok0 + BMT < a.T ? tok0 + BMT : a.T) - 1;
+  const int i_min = a.n + tok0, i_max = a.n + blk_last;
+
+  // ---- key tiles visited by this block --------------------------------------
+  int n1, w0, ntiles;
+  if constexpr (MODE == MODE_STREAMING) {
+    const int lo = i_min - a.R + 1 > 0 ? i_min - a.R + 1 : 0;
+    const int sink_hi = a.S < i_max + 1 ? a.S : i_max + 1;
+    n1 = (sink_hi + kBN - 1) / kBN;  // sink tiles cover [0, 64*n1)
+    w0 = lo > kBN * n1 ? lo : kBN * n1;
+    const int n2 = i_max >= w0 ? (i_max - w0) / kBN + 1 : 0;
+    ntiles = n1 + n2;
+  } else {
+    n1 = 0;
+    w0 = 0;
+    ntiles = i_max / kBN + 1;
+  }
+  auto tile_pos = [&](int k) { return k < n1 ? kBN * k : w0 + kBN * (k - n1); };
+
+  // ---- query fragments (B operand of S^T = K Q^T) ----------------------------
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = a.q + (((int64_t)b * a.T + t_qc) * a.Hq + head) * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qp + 16 * ks));
+  }
+
+  // ---- global -> register staging of one K/V tile ------------------------------
+  const int kr_row = tid >> 2, kr_d0 = (tid & 3) * (D / 4);
+  const int vg = tid & 15, vdc = tid >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
+  const bool v_active = vdc < D / 8;
+  u32x4 kreg[KLD], vreg[4];
+  auto load_tile = [&](int p0) {
+    const uint16_t* kp = KeySrc<D>::template row<MODE>(a, b, kv, p0 + kr_row, false) + kr_d0;
+#pragma unroll
+    for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
+    if (v_active) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = ld16(KeySrc<D>::template row<MODE>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < KLD; ++c) st16(Ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+    if (v_active) {
+      const uint32_t* w0p = &vreg[0].x;
+      const uint32_t* w1p = &vreg[1].x;
+      const uint32_t* w2p = &vreg[2].x;
+      const uint32_t* w3p = &vreg[3].x;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int d = 8 * vdc + i;
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t lo = __builtin_amdgcn_perm(w1p[i >> 1], w0p[i >> 1], sel);
+        uint32_t hi = __builtin_amdgcn_perm(w3p[i >> 1], w2p[i >> 1], sel);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + d * kBN + 4 * (vg ^ (d & 15)));
+        dst[0] = lo;
+        dst[1] = hi;
+      }
+    }
+  };
+
+  // ---- state --------------------------------------------------------------------
+  f32x16 o_f[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
+  float m_f = -INFINITY, l_f = 0.0f;
+  f32x16 o_l[kMixed ? DB : 1];
+  float m_l = -INFINITY, l_l = 0.0f;
+  if constexpr (kMixed) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o_l[db] = f32x16{};
+  }
+
+  // one online-softmax update of (m, l, O) from masked log2-domain scores;
+  // returns P packed as the B operands of the four 16-key slices
+  auto softmax_update = [&](const float (&sc)[2][16], float& m, float& l, f32x16 (&O)[DB],
+                            bf16x8 (&pb)[4]) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sc[kb][j]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    const float mn = fmaxf(m, tm);
+    const float ms = mn == -INFINITY ? 0.0f : mn;  // no allowed key yet
+    const float corr = fast_exp2(m - ms);
+    m = mn;
+    float ls = 0.0f;
+    float p[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        p[kb][j] = fast_exp2(sc[kb][j] - ms);
+        ls += p[kb][j];
+      }
+    l = l * corr + ls;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] *= corr;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)p[s >> 1][8 * (s & 1) + i];
+  };
+  auto pv = [&](const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 32 * db + q32;
+        const int sw = d & 15;
+        const uint16_t* row = Vt + d * kBN;
+        const uint2 x = *reinterpret_cast<const uint2*>(row + 4 * ((4 * s + h2) ^ sw));
+        const uint2 y = *reinterpret_cast<const uint2*>(row + 4 * ((4 * s + 2 + h2) ^ sw));
+        const bf16x8 av = as_bf16x8(u32x4{x.x, x.y, y.x, y.y});
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[s], O[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop ----------------------------------------------------------------
+  load_tile(tile_pos(0));
+  store_tile();
+  __syncthreads();
+  for (int k = 0; k < ntiles; ++k) {
+    const int p0 = tile_pos(k);
+    const bool more = k + 1 < ntiles;
+    if (more) load_tile(tile_pos(k + 1));
+
+    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = f32x16{};
+      const uint16_t* krow = Ks + (32 * kb + q32) * KPAD + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], st[kb], 0, 0, 0);
+      }
+    }
+    // scores in the log2 domain with this mode's mask
+    float sf[2][16];
+    float sl[2][16];
+    const bool lam_tile = kMixed && (p0 < a.S || p0 + kBN - 1 >= i_min - a.R + 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
+        const float x = st[kb][j] * a.scale_log2;
+        const bool causal = jp <= i_q;
+        const bool lam = causal && (jp < a.S || i_q - jp < a.R);
+        if constexpr (MODE == MODE_STREAMING) {
+          sf[kb][j] = lam ? x : -INFINITY;
+        } else {
+          sf[kb][j] = causal ? x : -INFINITY;
+          if constexpr (kMixed) sl[kb][j] = lam ? x : -INFINITY;
+        }
+      }
+    bf16x8 pb[4];
+    softmax_update(sf, m_f, l_f, o_f, pb);
+    pv(pb, o_f);
+    if constexpr (kMixed) {
+      if (lam_tile) {
+        bf16x8 pl[4];
+        softmax_update(sl, m_l, l_l, o_l, pl);
+        pv(pl, o_l);
+      }
+    }
+    __syncthreads();  // every wave is done with this tile's LDS
+    if (more) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue -----------------------------------------------------------------
+  if (t_q >= a.T) return;
+  const float lf = l_f + __shfl_xor(l_f, 32, 64);
+  float wf = 1.0f / lf, wl = 0.0f;
+  if constexpr (kMixed) {
+    const float al = a.alpha[kv];
+    const float ll = l_l + __shfl_xor(l_l, 32, 64);
+    wf = al / lf;
+    wl = (1.0f - al) / ll;
+  }
+  uint16_t* op = a.out + (((int64_t)b * a.T + t_q) * a.Hq + head) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = o_f[db][4 * jb + r] * wf;
+        if constexpr (kMixed) v[r] = fmaf(o_l[db][4 * jb + r], wl, v[r]);
+      }
+      uint2 w;
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(op + 32 * db + 8 * jb + 4 * h2) = w;
+    }
+}
+
+// ---- launchers -------------------------------------------------------------------
+template <int D, int HB, int MODE>
+static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
+  constexpr int BMT = 32 * 4 / HB;
+  AttnArgs x = a;
+  x.n_qtiles = (a.T + BMT - 1) / BMT;
+  dim3 grid((unsigned)x.n_qtiles, (unsigned)(n_kv * (a.G / HB)), (unsigned)B);
+  attn_kernel<D, HB, MODE><<<grid, 256, 0, s>>>(x);
+  return hipGetLastError();
+}
+
+template <int D, int MODE>
+static hipError_t launch_d(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
+  switch (a.G) {
+    case 1: return launch_hb<D, 1, MODE>(a, n_kv, B, s);
+    case 2: return launch_hb<D, 2, MODE>(a, n_kv, B, s);
+    default: return launch_hb<D, 4, MODE>(a, n_kv, B, s);  // G = 4 or 8
+  }
+}
+
+template <int MODE>
+static hipError_t launch_mode(const AttnArgs& a, int D, int n_kv, int B, hipStream_t s) {
+  if (n_kv <= 0 || a.T <= 0) return hipSuccess;
+  return D == 128 ? launch_d<128, MODE>(a, n_kv, B, s) : launch_d<64, MODE>(a, n_kv, B, s);
+}
+
+static AttnArgs base_args(const duo_layer* L, const void* q, int T, void* out) {
+  const duo_layer_desc& d = L->d;
+  AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.T = T;
+  a.Hq = d.n_q_heads;
+  a.Hkv = d.n_kv_heads;
+  a.Hr = L->Hr;
+  a.Hs = L->Hs;
+  a.G = L->G;
+  a.S = d.sink;
+  a.R = d.recent;
+  a.cap = d.retrieval_capacity;
+  a.n = (int)L->n;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  a.kc = reinterpret_cast<const uint16_t*>(L->rbuf + L->lay.k_offset);
+  a.vc = reinterpret_cast<const uint16_t*>(L->rbuf + L->lay.v_offset);
+  a.kr = reinterpret_cast<const uint16_t*>(L->sbuf + L->lay.ring_k_offset);
+  a.vr = reinterpret_cast<const uint16_t*>(L->sbuf + L->lay.ring_v_offset);
+  return a;
+}
+
+hipError_t launch_prefill_retrieval(const duo_layer* L, const void* q, int T, void* out,
+                                    hipStream_t s) {
+  AttnArgs a = base_args(L, q, T, out);
+  a.kv_base = 0;
+  return launch_mode<MODE_RETRIEVAL>(a, L->d.head_dim, L->Hr, L->d.batch, s);
+}
+
+hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const void* k,
+                                    const void* v, int T, void* out, hipStream_t s) {
+  AttnArgs a = base_args(L, q, T, out);
+  a.k_in = static_cast<const uint16_t*>(k);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.kv_base = L->Hr;
+  return launch_mode<MODE_STREAMING>(a, L->d.head_dim, L->Hs, L->d.batch, s);
+}
+
+hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, const void* v,
+                        const float* alpha, int T, void* out, hipStream_t s) {
+  AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.k_in = static_cast<const uint16_t*>(k);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.alpha = alpha;
+  a.T = T;
+  a.Hq = d.n_q_heads;
+  a.Hkv = d.n_kv_heads;
+  a.G = d.n_q_heads / d.n_kv_heads;
+  a.S = d.sink;
+  a.R = d.recent;
+  a.n = 0;
+  a.kv_base = 0;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  return launch_mode<MODE_MIXED>(a, d.head_dim, d.n_kv_heads, d.batch, s);
+}
+
+}  // namespace duo

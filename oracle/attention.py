@@ -105,21 +105,23 @@ def streaming_attention(q, k, v, scale: float, sink: int = 16, recent: int = 64,
 
 
 def mixed_attention(q, k, v, alpha, scale: float, sink: int = 16, recent: int = 64,
-                    heads=None) -> np.ndarray:
+                    heads=None, rows=None) -> np.ndarray:
     """Gate-blended forward used for head identification:
     o_h = alpha[h // G] * full_h + (1 - alpha[h // G]) * streaming_h.
-    q [T,Hq,D], k/v [T,Hkv,D], alpha [Hkv]; returns float64 [T,Hq,D]."""
+    q [T,Hq,D], k/v [T,Hkv,D], alpha [Hkv]; returns float64 [T,Hq,D].
+    ``heads`` / ``rows`` restrict the query heads / rows computed (others NaN)."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, D = q.shape
     Hkv = np.asarray(k).shape[1]
     G = _group(Hq, Hkv)
     pos = np.arange(T)
+    rows = pos if rows is None else np.asarray(rows)
     out = np.full((T, Hq, D), np.nan)
     for h in (range(Hq) if heads is None else heads):
         kv = h // G
         a = float(alpha[kv])
-        full = masked_attention(q[:, h], k[:, kv], v[:, kv], pos, pos, scale, "full")
-        stream = masked_attention(q[:, h], k[:, kv], v[:, kv], pos, pos, scale,
+        full = masked_attention(q[rows, h], k[:, kv], v[:, kv], rows, pos, scale, "full")
+        stream = masked_attention(q[rows, h], k[:, kv], v[:, kv], rows, pos, scale,
                                   "streaming", sink, recent)
-        out[:, h] = a * full + (1.0 - a) * stream
+        out[rows, h] = a * full + (1.0 - a) * stream
     return out

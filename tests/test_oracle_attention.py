@@ -215,3 +215,14 @@ def test_no_allowed_key_is_an_error():
     with pytest.raises(ValueError):
         oracle.masked_attention(np.zeros((1, 2)), np.zeros((1, 2)), np.zeros((1, 2)),
                                 [0], [5], 1.0, "full")
+
+
+def test_mixed_rows_subset_matches_all_rows():
+    g = rng(13)
+    T, H, D = 100, 2, 4
+    q, k, v = (normal(g, (T, H, D)).astype(np.float64) for _ in range(3))
+    full = oracle.mixed_attention(q, k, v, [0.3, 0.8], 0.5, 3, 7)
+    rows = [0, 17, 99]
+    part = oracle.mixed_attention(q, k, v, [0.3, 0.8], 0.5, 3, 7, rows=rows)
+    np.testing.assert_array_equal(part[rows], full[rows])
+    assert np.isnan(part[1]).all()
