@@ -13,12 +13,14 @@ from U(0,1). N(0,1) inputs give diffuse attention; the needle inputs below add
 one sharply peaked key for routing checks.
 
 Recipe (host path). ``numpy.random.Generator(PCG64(seed))`` with
-``seed = 1000 + config index`` draws, in this order: Q, K, V of the prefill or
-context (token-major ``[T, H, D]``), then the per-step q, k, v of the decode
-steps (``[steps, H, D]`` each), then alpha, then the retrieval-head choice
-``sorted(permutation(H_kv)[:H_r])``. Values are float32 standard normals rounded
-to bf16 (round-to-nearest-even) or, for the fp16 KV of the 1M-token int4 decode
-workload, to fp16.
+``seed = 1000 + config index`` draws, in this order: Q of the prefill or mixed
+sequence (token-major ``[T, Hq, D]``); K and V of the prefill or context in
+chunks of 65536 tokens (K chunk, then V chunk, ``[n, Hkv, D]`` each); the
+per-step q, k, v of the decode steps (``[steps, H, D]`` each); alpha; then the
+retrieval-head choice ``sorted(permutation(H_kv)[:H_r])``. Values are float32
+standard normals rounded to bf16 (round-to-nearest-even) or, for the fp16 KV of
+the 1M-token int4 decode workload, to fp16. ``ContextStream`` yields the same
+sequence chunk by chunk for contexts too large to hold at once.
 
 Recipe (device path, bench-scale only). ``torch.Generator(device=...)`` seeded
 with the same seed fills large context tensors directly in HBM; such data is
@@ -163,6 +165,56 @@ class LayerInputs:
     extra: dict = field(default_factory=dict)
 
 
+KV_CHUNK = 65536
+
+
+class ContextStream:
+    """The draw sequence of ``make_inputs``, produced chunk by chunk.
+
+    Iterate ``chunks()`` to get (k, v) context/prefill chunks of up to
+    ``KV_CHUNK`` tokens, then call ``tail()`` for the decode steps, alpha and
+    the retrieval mask (in that draw order). ``q`` (prefill/mixed Q) is drawn
+    up front."""
+
+    def __init__(self, w: Workload, *, tokens: Optional[int] = None,
+                 steps: Optional[int] = None, n_q_heads: Optional[int] = None,
+                 seed: Optional[int] = None):
+        self.w = w
+        self.gen = rng(SEED_BASE + w.index if seed is None else seed)
+        self.hq = w.n_q_heads if n_q_heads is None else n_q_heads
+        self.T = tokens if tokens is not None else (w.prefill_tokens or w.context or w.mixed_tokens)
+        self.steps = steps if steps is not None else w.decode_steps
+        self.kv_round = round_fp16 if w.ring_dtype == "fp16" else round_bf16
+        self.q = None
+        if self.T and (w.prefill_tokens or w.mixed_tokens):
+            self.q = round_bf16(normal(self.gen, (self.T, self.hq, w.head_dim))
+                                * np.float32(w.q_prescale))
+
+    def chunks(self):
+        hkv, D = self.w.n_kv_heads, self.w.head_dim
+        for a in range(0, self.T, KV_CHUNK):
+            n = min(KV_CHUNK, self.T - a)
+            k = self.kv_round(normal(self.gen, (n, hkv, D)))
+            v = self.kv_round(normal(self.gen, (n, hkv, D)))
+            yield k, v
+
+    def tail(self, out: "LayerInputs") -> "LayerInputs":
+        w, gen = self.w, self.gen
+        hkv, D = w.n_kv_heads, w.head_dim
+        if self.steps:
+            out.q_steps = round_bf16(normal(gen, (self.steps, self.hq, D)) * np.float32(w.q_prescale))
+            out.k_steps = self.kv_round(normal(gen, (self.steps, hkv, D)))
+            out.v_steps = self.kv_round(normal(gen, (self.steps, hkv, D)))
+        if w.mixed_tokens:
+            out.alpha = gen.uniform(0.0, 1.0, size=hkv).astype(np.float32)
+        if w.fixed_retrieval is not None:
+            heads = list(w.fixed_retrieval)
+        else:
+            heads = choose_retrieval(gen, hkv, w.n_retrieval_kv)
+        out.retrieval_mask = retrieval_mask_from_heads(hkv, heads)
+        return out
+
+
 def make_inputs(w: Workload, *, tokens: Optional[int] = None,
                 steps: Optional[int] = None, n_q_heads: Optional[int] = None,
                 seed: Optional[int] = None) -> LayerInputs:
@@ -170,35 +222,15 @@ def make_inputs(w: Workload, *, tokens: Optional[int] = None,
 
     ``tokens``/``steps`` override the prefill/context length and the decode
     step count (smaller cases of the same structure); the draw order is the
-    one stated in the module docstring. Activation values are rounded to the
-    storage type the kernels read: bf16, or fp16 for the KV of a workload
-    whose ring is fp16.
+    one stated in the module docstring.
     """
-    gen = rng(SEED_BASE + w.index if seed is None else seed)
-    hq = w.n_q_heads if n_q_heads is None else n_q_heads
-    hkv = w.n_kv_heads
-    D = w.head_dim
-    T = tokens if tokens is not None else (w.prefill_tokens or w.context or w.mixed_tokens)
-    n_steps = steps if steps is not None else w.decode_steps
-    kv_round = round_fp16 if w.ring_dtype == "fp16" else round_bf16
-    out = LayerInputs(workload=w, retrieval_mask=np.zeros(hkv, np.uint8))
-    if T:
-        if w.prefill_tokens or w.mixed_tokens:
-            out.q = round_bf16(normal(gen, (T, hq, D)) * np.float32(w.q_prescale))
-        out.k = kv_round(normal(gen, (T, hkv, D)))
-        out.v = kv_round(normal(gen, (T, hkv, D)))
-    if n_steps:
-        out.q_steps = round_bf16(normal(gen, (n_steps, hq, D)) * np.float32(w.q_prescale))
-        out.k_steps = kv_round(normal(gen, (n_steps, hkv, D)))
-        out.v_steps = kv_round(normal(gen, (n_steps, hkv, D)))
-    if w.mixed_tokens:
-        out.alpha = gen.uniform(0.0, 1.0, size=hkv).astype(np.float32)
-    if w.fixed_retrieval is not None:
-        heads = list(w.fixed_retrieval)
-    else:
-        heads = choose_retrieval(gen, hkv, w.n_retrieval_kv)
-    out.retrieval_mask = retrieval_mask_from_heads(hkv, heads)
-    return out
+    cs = ContextStream(w, tokens=tokens, steps=steps, n_q_heads=n_q_heads, seed=seed)
+    out = LayerInputs(workload=w, retrieval_mask=np.zeros(w.n_kv_heads, np.uint8), q=cs.q)
+    if cs.T:
+        ks, vs = zip(*cs.chunks())
+        out.k = ks[0] if len(ks) == 1 else np.concatenate(ks)
+        out.v = vs[0] if len(vs) == 1 else np.concatenate(vs)
+    return cs.tail(out)
 
 
 def random_case(seed: int, *, T: int, n_q_heads: int, n_kv_heads: int, head_dim: int,

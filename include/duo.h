@@ -77,18 +77,22 @@ typedef struct {
   int32_t recent;               /* R >= 1 recent tokens incl. the query (64) */
   int64_t retrieval_capacity;   /* max tokens held by the retrieval cache */
   duo_dtype kv_dtype;           /* dtype of k/v inputs and of the ring: BF16 | FP16 */
-  duo_dtype retrieval_dtype;    /* kv_dtype, or INT4_G32 */
+  duo_dtype retrieval_dtype;    /* kv_dtype, or INT4_G32 (then Hq/Hkv * D/32 <= 16) */
   float softmax_scale;          /* multiplies q.k before the softmax */
 } duo_layer_desc;
 
 /* Byte offsets of the arrays inside the caller-provided buffers.
  * Retrieval buffer, kv_dtype cache:
  *   K  [B][Hr][cap][D] elements at k_offset, V likewise at v_offset.
- * Retrieval buffer, INT4_G32 cache:
- *   K codes [B][Hr][cap][D/2] bytes at k_offset (byte b of a row holds
- *   channel 2b in its low nibble and 2b+1 in its high nibble), V codes at
- *   v_offset, K scale/zero [B][Hr][cap][D/32][2] fp16 (scale, zero) at
- *   k_sz_offset, V at v_sz_offset.
+ * Retrieval buffer, INT4_G32 cache (cap32 = capacity rounded up to 32):
+ *   K codes [B][Hr][cap32][D/2] bytes at k_offset, token-major: byte b of a
+ *   row holds channel 2b in its low nibble and 2b+1 in its high nibble.
+ *   V codes [B][Hr][cap32/32][D][16] bytes at v_offset, in 32-token blocks:
+ *   byte m of channel row d of a block holds token m of the block in its low
+ *   nibble and token m+16 in its high nibble.
+ *   K scale/zero [B][Hr][cap32][D/32][2] fp16 (scale, zero) at k_sz_offset,
+ *   V scale/zero likewise at v_sz_offset. A value decodes as
+ *   fma(code, scale, zero) in fp32.
  * Streaming buffer: ring K [B][Hs][S+R][D] kv_dtype at ring_k_offset, ring V
  *   at ring_v_offset, Hs = Hkv - Hr. Token position p lives in slot p if
  *   p < S, else in slot S + ((p - S) mod R).
@@ -134,7 +138,9 @@ duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t
  * append the chunk to their cache and attend causally over positions
  * [0, n+chunk_len); streaming heads attend under the Lambda mask over the ring
  * as it was before the chunk plus the chunk, then the ring is updated.
- * Writes out [B, chunk_len, Hq, D] bf16 and advances the token count. */
+ * Writes out [B, chunk_len, Hq, D] bf16 and advances the token count.
+ * Layers whose kv_dtype or retrieval_dtype is not BF16 return
+ * DUO_ERR_UNSUPPORTED (fill such caches with duo_append_kv). */
 duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,
                              int32_t chunk_len, void* out, hipStream_t stream);
 

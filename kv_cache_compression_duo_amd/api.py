@@ -132,12 +132,17 @@ class DuoLayer:
                 _bytes_view(self.rbuf, self.layout.v_offset, shape, dt))
 
     def retrieval_int4(self):
-        """(K codes, V codes [B,Hr,cap,D/2] u8, K sz, V sz [B,Hr,cap,D/32,2] fp16)."""
+        """Views of a 4-bit retrieval cache (cap32 = capacity rounded up to 32):
+        K codes [B,Hr,cap32,D/2] u8 (token-major), V codes
+        [B,Hr,cap32/32,D,16] u8 (32-token blocks, byte m of a channel row =
+        token m | token m+16 << 4), K and V scale/zero [B,Hr,cap32,D/32,2] fp16."""
         assert self.retrieval_dtype == "int4"
-        cs = (self.B, self.Hr, self.capacity, self.D // 2)
-        ss = (self.B, self.Hr, self.capacity, self.D // 32, 2)
-        return (_bytes_view(self.rbuf, self.layout.k_offset, cs, torch.uint8),
-                _bytes_view(self.rbuf, self.layout.v_offset, cs, torch.uint8),
+        cap32 = (self.capacity + 31) // 32 * 32
+        ks = (self.B, self.Hr, cap32, self.D // 2)
+        vs = (self.B, self.Hr, cap32 // 32, self.D, 16)
+        ss = (self.B, self.Hr, cap32, self.D // 32, 2)
+        return (_bytes_view(self.rbuf, self.layout.k_offset, ks, torch.uint8),
+                _bytes_view(self.rbuf, self.layout.v_offset, vs, torch.uint8),
                 _bytes_view(self.rbuf, self.layout.k_sz_offset, ss, torch.float16),
                 _bytes_view(self.rbuf, self.layout.v_sz_offset, ss, torch.float16))
 

@@ -22,7 +22,7 @@ SOURCES = [
     "k_append.hip",
     "k_decode.hip",
     "k_attn.hip",
-    "k_stubs.hip",
+    "k_decode_int4.hip",
 ]
 
 ARCH = os.environ.get("DUO_OFFLOAD_ARCH", "gfx950")

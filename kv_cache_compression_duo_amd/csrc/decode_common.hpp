@@ -1,0 +1,184 @@
+// Building blocks shared by the decode kernels: per-wave streaming attention
+// over rows of a bf16/fp16 KV source (16-byte loads, D/8 lanes per row, G query
+// heads per KV head sharing every load) and the merge of the waves' softmax
+// states through LDS.
+#pragma once
+#include "device_common.hpp"
+
+namespace duo {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 32;  // rows per wave-tile
+
+// Per-wave online-softmax state for G query heads over 8 channels per lane.
+template <int G>
+struct WaveState {
+  float m[G], l[G], acc[G][8];
+};
+
+// Attend over rows [r0, r1) of a KV source, tiles interleaved across the
+// block's waves, with the next tile's K/V loads in flight while the current
+// tile is computed. kptr/vptr(row) return the 16-byte-aligned base of a row.
+// On return l and acc are summed over the wave's rows (every lane holds the
+// totals for its 8 channels); m is the wave's running maximum.
+template <int D, int G, typename Tag, typename KPtr, typename VPtr>
+__device__ __forceinline__ void attend_rows(WaveState<G>& st, const float (&qf)[G][8], int r0,
+                                            int r1, KPtr kptr, VPtr vptr) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPL = 64 / LPR;    // rows per load
+  constexpr int U = kTile / RPL;   // loads per tile
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lc = lane % LPR, lr = lane / LPR;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.acc[g][c] = 0.0f;
+  }
+  int t0 = r0 + wave * kTile;
+  if (t0 >= r1) return;
+  // Loads are unconditional (rows past the range are clamped to the last
+  // valid row and masked out of the softmax), so the tile loop is straight-line
+  // code and the next tile's loads stay in flight during the current compute.
+  auto load = [&](u32x4 (&kb)[U], u32x4 (&vb)[U], int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int row = base + u * RPL + lr;
+      row = row < r1 ? row : r1 - 1;
+      kb[u] = ld16_nt(kptr(row) + lc * 8);
+      vb[u] = ld16_nt(vptr(row) + lc * 8);
+    }
+  };
+  auto compute = [&](const u32x4 (&kb)[U], const u32x4 (&vb)[U], int base) {
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+      unpack8<Tag>(kb[u], kf);
+      const int row = base + u * RPL + lr;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a = fmaf(qf[g][c], kf[c], a);
+        a = group_sum<LPR>(a);
+        s[u][g] = row < r1 ? a : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float tm = s[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) tm = fmaxf(tm, s[u][g]);
+      if constexpr (LPR == 8) tm = fmaxf(tm, dpp<0x128>(tm));  // row_ror:8 == xor 8
+      tm = fmaxf(tm, xor_lane(tm, 16));
+      tm = fmaxf(tm, xor_lane(tm, 32));
+      const float mn = fmaxf(st.m[g], tm);
+      const float corr = fast_exp2(st.m[g] - mn);
+      st.m[g] = mn;
+      float ls = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[g][c] *= corr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = fast_exp2(s[u][g] - mn);
+        s[u][g] = p;
+        ls += p;
+      }
+      st.l[g] = st.l[g] * corr + ls;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      unpack8<Tag>(vb[u], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st.acc[g][c] = fmaf(s[u][g], vf[c], st.acc[g][c]);
+    }
+  };
+  // Ping-pong register buffers; the prefetch is issued even past the end (all
+  // rows then clamp to the last valid row, a cached re-read) so that the
+  // waits before each compute only cover the tile being computed.
+  constexpr int stride = kWaves * kTile;
+  u32x4 ka[U], va[U], kb[U], vb[U];
+  load(ka, va, t0);
+  for (;;) {
+    const int t1 = t0 + stride;
+    load(kb, vb, t1);
+    compute(ka, va, t0);
+    if (t1 >= r1) break;
+    t0 = t1 + stride;
+    load(ka, va, t0);
+    compute(kb, vb, t1);
+    if (t0 >= r1) break;
+  }
+  // Sum l and acc over the row groups of the wave (lanes sharing lc).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if constexpr (LPR == 8) {
+      st.l[g] += dpp<0x128>(st.l[g]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[g][c] += dpp<0x128>(st.acc[g][c]);
+    }
+    st.l[g] += xor_lane(st.l[g], 16);
+    st.l[g] += xor_lane(st.l[g], 32);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      st.acc[g][c] += xor_lane(st.acc[g][c], 16);
+      st.acc[g][c] += xor_lane(st.acc[g][c], 32);
+    }
+  }
+}
+
+// Merge the waves' states through LDS. On return, thread t < G*D/8... holds
+// nothing; the merged (m, l, acc[D]) per head is left in LDS `red`.
+template <int D, int G>
+struct BlockRed {
+  float m[kWaves][G], l[kWaves][G], acc[kWaves][G][D];
+  float M[G], L[G];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void block_merge(BlockRed<D, G>& red, const WaveState<G>& st) {
+  constexpr int LPR = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) red.acc[wave][g][lane * 8 + c] = st.acc[g][c];
+      if (lane == 0) {
+        red.m[wave][g] = st.m[g];
+        red.l[wave][g] = st.l[g];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    int g = threadIdx.x;
+    float M = red.m[0][g];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red.m[w][g]);
+    float Lsum = 0.0f;
+    for (int w = 0; w < kWaves; ++w)
+      Lsum += red.l[w][g] * (red.m[w][g] == -INFINITY ? 0.0f : fast_exp2(red.m[w][g] - M));
+    red.M[g] = M;
+    red.L[g] = Lsum;
+  }
+  __syncthreads();
+  // merged acc, in place into red.acc[0]
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    int g = i / D, dd = i % D;
+    float M = red.M[g];
+    float a = 0.0f;
+    for (int w = 0; w < kWaves; ++w)
+      if (red.m[w][g] != -INFINITY) a += red.acc[w][g][dd] * fast_exp2(red.m[w][g] - M);
+    red.acc[0][g][dd] = a;
+  }
+  __syncthreads();
+}
+
+}  // namespace duo

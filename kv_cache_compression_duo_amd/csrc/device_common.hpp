@@ -26,6 +26,16 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return u32x4{r.x, r.y, r.z, r.w};
 }
 
+// Word i (0..3) and 16-bit half i (0..7) of a 16-byte vector, by value (no
+// pointer reinterpretation of the struct).
+__device__ __forceinline__ uint32_t word_of(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
+  const uint32_t w = word_of(v, i >> 1);
+  return (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
 // ---- element types ---------------------------------------------------------
 struct Bf16Tag {};
 struct Fp16Tag {};

@@ -55,6 +55,9 @@ static duo_status check_desc(const duo_layer_desc* d) {
   if (d->retrieval_dtype != d->kv_dtype && d->retrieval_dtype != DUO_INT4_G32)
     return DUO_ERR_UNSUPPORTED;
   if (!isfinite(d->softmax_scale)) return DUO_ERR_INVALID_ARG;
+  // the 4-bit decode kernel maps (query head, channel group) pairs of a KV
+  // head onto the 16 columns of one MFMA tile
+  if (d->retrieval_dtype == DUO_INT4_G32 && G * (d->head_dim / 32) > 16) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -74,8 +77,9 @@ duo_status duo_layer_layout(const duo_layer_desc* d, duo_layout* out) {
   duo_layout L;
   memset(&L, 0, sizeof(L));
   if (d->retrieval_dtype == DUO_INT4_G32) {
-    size_t codes = align_up(B * Hr * cap * (D / 2), 256);
-    size_t sz = align_up(B * Hr * cap * (D / 32) * 2 * 2, 256);
+    const size_t cap32 = (size_t)cap32_of(d->retrieval_capacity);
+    size_t codes = align_up(B * Hr * cap32 * (D / 2), 256);
+    size_t sz = align_up(B * Hr * cap32 * (D / 32) * 2 * 2, 256);
     L.k_offset = 0;
     L.v_offset = codes;
     L.k_sz_offset = 2 * codes;

@@ -23,6 +23,8 @@ namespace duo {
 constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+// 4-bit caches are allocated in whole 32-token blocks.
+inline int64_t cap32_of(int64_t cap) { return (cap + 31) / 32 * 32; }
 
 struct WsView {
   uint32_t* counters;

@@ -70,35 +70,71 @@ __device__ __forceinline__ void encode_group_part(const u32x4& raw, uint32_t* co
             ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
 }
 
-// One thread per 8 channels; the thread count per (b,t,h) row is D/8, a
-// multiple of 4, so the 4 lanes of a group are always in one quad.
+// 4-bit cache append. Key codes are token-major ([cap32][D/2] bytes, byte b of
+// a row = channel 2b | channel 2b+1 << 4). Value codes are stored in 32-token
+// blocks [cap32/32][D][16 bytes] where byte m of a channel row holds token m
+// of the block in its low nibble and token m + 16 in its high nibble (the
+// operand order of the decode kernel's PV product). A thread owns one byte
+// position m of a block (tokens m and m + 16) and 8 channels, so no two
+// threads write the same byte; a byte whose other token lies outside the
+// appended range is read, modified and written by its one owner. Scale and
+// zero-point words are [cap32][D/32] (fp16 s | fp16 z << 16).
+// Thread order: channel chunk fastest, so the 4 lanes of a quad hold one
+// 32-channel group of one token (the min/max reduction uses quad DPP).
 template <typename Tag>
 __global__ void append_int4_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
-                                   uint32_t* __restrict__ kcodes, uint32_t* __restrict__ vcodes,
+                                   uint32_t* __restrict__ kcodes, uint8_t* __restrict__ vcodes,
                                    uint32_t* __restrict__ ksz, uint32_t* __restrict__ vsz, int B,
-                                   int T, int Hkv, int Hr, int chunks, int64_t cap, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t total = (int64_t)B * T * Hr * chunks;
-  // Every lane of a quad is either in range or not (total is a multiple of 4),
-  // so the DPP exchanges below never read an inactive lane.
-  if (i >= total) return;
-  int c = (int)(i % chunks);
+                                   int T, int Hkv, int Hr, int chunks, int64_t cap32, int64_t n,
+                                   int64_t blk0, int nblk) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * Hr * nblk * 16 * chunks;
+  if (i >= total) return;  // whole quads: total and blockDim are multiples of 4
+  const int c = (int)(i % chunks);
   int64_t r = i / chunks;
-  int h = (int)(r % Hr);
-  r /= Hr;
-  int t = (int)(r % T);
-  int b = (int)(r / T);
-  int64_t src = (((int64_t)b * T + t) * Hkv + h) * chunks + c;
-  int64_t row = ((int64_t)b * Hr + h) * cap + n + t;
-  uint32_t kq, ks, vq, vs;
-  encode_group_part<Tag>(k[src], &kq, &ks);
-  encode_group_part<Tag>(v[src], &vq, &vs);
-  kcodes[row * chunks + c] = kq;  // 8 nibbles = 4 bytes per thread
-  vcodes[row * chunks + c] = vq;
-  if ((c & 3) == 0) {
-    int groups = chunks / 4;
-    ksz[row * groups + c / 4] = ks;
-    vsz[row * groups + c / 4] = vs;
+  const int m = (int)(r % 16);
+  r /= 16;
+  const int64_t blk = blk0 + r % nblk;
+  r /= nblk;
+  const int h = (int)(r % Hr);
+  const int b = (int)(r / Hr);
+  const int64_t hb = (int64_t)b * Hr + h;
+  const int groups = chunks / 4;
+  const int D = chunks * 8;
+  uint32_t vq[2] = {0u, 0u};
+  bool in[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t p = blk * 32 + m + 16 * e;
+    in[e] = p >= n && p < n + T;  // uniform over the quad (same token)
+    if (in[e]) {
+      const int64_t src = (((int64_t)b * T + (p - n)) * Hkv + h) * chunks + c;
+      uint32_t kq, ks, vs;
+      encode_group_part<Tag>(k[src], &kq, &ks);
+      encode_group_part<Tag>(v[src], &vq[e], &vs);
+      const int64_t row = hb * cap32 + p;
+      kcodes[row * chunks + c] = kq;
+      if ((c & 3) == 0) {
+        ksz[row * groups + c / 4] = ks;
+        vsz[row * groups + c / 4] = vs;
+      }
+    }
+  }
+  if (!in[0] && !in[1]) return;  // this byte pair lies outside the appended range
+  // value codes: channel rows 8c .. 8c+7 of block blk, byte m
+  uint8_t* vb = vcodes + ((hb * (cap32 / 32) + blk) * D + 8 * c) * 16 + m;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint8_t* dst = vb + 16 * j;
+    const uint32_t lo = (vq[0] >> (4 * j)) & 0xFu, hi = (vq[1] >> (4 * j)) & 0xFu;
+    uint32_t byte;
+    if (in[0] && in[1]) {
+      byte = lo | (hi << 4);
+    } else {
+      const uint32_t old = *dst;
+      byte = in[0] ? (old & 0xF0u) | lo : (old & 0x0Fu) | (hi << 4);
+    }
+    *dst = (uint8_t)byte;
   }
 }
 
@@ -150,18 +186,23 @@ hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v,
   if (total == 0) return hipSuccess;
   unsigned grid = blocks_for(total, 256);
   if (d.retrieval_dtype == DUO_INT4_G32) {
+    const int64_t cap32 = cap32_of(d.retrieval_capacity);
+    const int64_t blk0 = L->n / 32, blk1 = (L->n + T - 1) / 32;
+    const int nblk = (int)(blk1 - blk0 + 1);
+    const int64_t tot = (int64_t)d.batch * L->Hr * nblk * 16 * chunks;
     auto* kq = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.k_offset);
-    auto* vq = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.v_offset);
+    auto* vq = reinterpret_cast<uint8_t*>(L->rbuf + L->lay.v_offset);
     auto* ks = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.k_sz_offset);
     auto* vs = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.v_sz_offset);
+    const unsigned g4 = blocks_for(tot, 256);
     if (d.kv_dtype == DUO_FP16)
-      append_int4_kernel<Fp16Tag><<<grid, 256, 0, s>>>(
+      append_int4_kernel<Fp16Tag><<<g4, 256, 0, s>>>(
           static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), kq, vq, ks, vs, d.batch, T,
-          d.n_kv_heads, L->Hr, chunks, d.retrieval_capacity, L->n);
+          d.n_kv_heads, L->Hr, chunks, cap32, L->n, blk0, nblk);
     else
-      append_int4_kernel<Bf16Tag><<<grid, 256, 0, s>>>(
+      append_int4_kernel<Bf16Tag><<<g4, 256, 0, s>>>(
           static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), kq, vq, ks, vs, d.batch, T,
-          d.n_kv_heads, L->Hr, chunks, d.retrieval_capacity, L->n);
+          d.n_kv_heads, L->Hr, chunks, cap32, L->n, blk0, nblk);
   } else {
     append_rows_kernel<<<grid, 256, 0, s>>>(
         static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),

@@ -165,16 +165,12 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
 #pragma unroll
     for (int c = 0; c < KLD; ++c) st16(Ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
     if (v_active) {
-      const uint32_t* w0p = &vreg[0].x;
-      const uint32_t* w1p = &vreg[1].x;
-      const uint32_t* w2p = &vreg[2].x;
-      const uint32_t* w3p = &vreg[3].x;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 8 * vdc + i;
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t lo = __builtin_amdgcn_perm(w1p[i >> 1], w0p[i >> 1], sel);
-        uint32_t hi = __builtin_amdgcn_perm(w3p[i >> 1], w2p[i >> 1], sel);
+        uint32_t lo = __builtin_amdgcn_perm(word_of(vreg[1], i >> 1), word_of(vreg[0], i >> 1), sel);
+        uint32_t hi = __builtin_amdgcn_perm(word_of(vreg[3], i >> 1), word_of(vreg[2], i >> 1), sel);
         uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + d * kBN + 4 * (vg ^ (d & 15)));
         dst[0] = lo;
         dst[1] = hi;
