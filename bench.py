@@ -1,16 +1,24 @@
 """Benchmark of the DuoAttention hot path on one MI355X.
 
-Default: the Llama-2-7B decode layer (MHA 32 heads x 128, bf16, 32768-token
-context, 8 retrieval heads, 24 streaming heads with a 16 + 64 ring). A step is
-one duo_decode call: the append of the new token to both caches, split-K
-retrieval attention over the full cache, streaming attention over the ring and
-the split merge -- one fused kernel launch.
+Headline (the JSON line's `value`): the Llama-2-7B decode layer -- MHA 32
+heads x 128, bf16, 32768-token context, 8 retrieval heads with the full cache,
+24 streaming heads with a 16 + 64 ring. A step is one duo_decode call (append
+of the new token to both caches, split-K retrieval attention, ring attention,
+split merge: one fused kernel launch). `value` is algorithmic KV GB/s (every
+cached K/V byte read once per step plus q/out/new-token traffic), `tok_per_s`
+the decode steps per second of this layer.
 
 The 134 MB retrieval cache of one layer fits in the 256 MB MALL, so the
-timed loop cycles over `--layers` independent layers (8 x 134 MB by default),
-as a model's decode step visits its layers; every step's KV bytes then come
-from HBM. Inputs are synthetic (seeded N(0,1) drawn on the device) and
-resident in HBM before the timed region. One JSON line is printed.
+timed loop cycles over `--layers` independent layers (8 x 134 MB), as a
+model's decode step visits its layers; every step's KV bytes then come from
+HBM. Inputs are synthetic (seeded N(0,1) drawn on the device) and resident in
+HBM before any timed region.
+
+The same line carries the other workloads under "workloads": the 8-head D=64
+layer (prefill 1024 + 16 decode steps, latency), the Llama-3-8B GQA chunked
+prefill (65536 tokens in 8192-token chunks, TFLOP/s), the alpha-blend mixed
+forward (Llama-2-7B shape, 16384 tokens, TFLOP/s) and the Llama-3-8B 4-bit
+decode at a 1,048,576-token context (KV GB/s, tok/s).
 
 `--gpus N` with N > 1 is refused: this build measures one GPU.
 """
@@ -30,15 +38,57 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 
 
-def _decode_step_bytes(n, Hr, Hs, Hq, Hkv, D, W, e=2):
-    """Algorithmic bytes of one decode step at position n: every cached K/V
-    byte read once, q read, out written, new K/V read and written once."""
-    retrieval = Hr * (n + 1) * D * 2 * e
-    streaming = Hs * min(n + 1, W) * D * 2 * e
-    return retrieval + streaming + Hq * D * 2 * 2 + Hkv * D * e * 2 * 2
+# ---- algorithmic work ------------------------------------------------------------
+def decode_step_bytes(n, Hr, Hs, Hq, Hkv, D, W, kv_bytes_per_token_head, ring_elem=2):
+    """Bytes one decode step at position n must move: every cached K/V byte
+    read once (retrieval rows 0..n, ring slots), q read, out written, the new
+    token's K/V read once and written once to its cache."""
+    retrieval = Hr * (n + 1) * kv_bytes_per_token_head
+    streaming = Hs * min(n + 1, W) * D * 2 * ring_elem
+    q_out = Hq * D * 2 * 2
+    new_read = Hkv * D * 2 * ring_elem
+    new_write = Hr * kv_bytes_per_token_head + Hs * D * 2 * ring_elem
+    return retrieval + streaming + q_out + new_read + new_write
 
 
-def bench_decode(args, dev):
+def causal_pairs(T0, T):
+    """Allowed (query, key) pairs of T causal queries at positions T0..T0+T-1."""
+    return T * T0 + T * (T + 1) // 2
+
+
+def lambda_pairs(T0, T, S, R):
+    """Allowed pairs under the Lambda mask (sink S, recent R incl. the query):
+    query i sees i + 1 keys while i + 1 <= S + R, else S + R keys."""
+    W = S + R
+    tot = 0
+    lo, hi = T0, T0 + T
+    a, b = lo, min(hi, W)
+    if b > a:
+        tot += (b * (b + 1) - a * (a + 1)) // 2
+    a = max(lo, W)
+    if hi > a:
+        tot += (hi - a) * W
+    return tot
+
+
+# ---- timing helpers --------------------------------------------------------------
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_region(torch, fn, reps=1):
+    a, b = _events(torch)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+# ---- workloads -------------------------------------------------------------------
+def bench_decode_llama2(args, dev):
     import torch
     import kv_cache_compression_duo_amd as duo
     from duo_synth import WORKLOADS, device_normal
@@ -53,7 +103,7 @@ def bench_decode(args, dev):
     for li in range(L):
         lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
                            capacity=ctx + per_layer, softmax_scale=w.softmax_scale, device=dev)
-        chunk = 4096
+        chunk = 8192
         for a in range(0, ctx, chunk):
             k = device_normal((1, chunk, Hkv, D), 7000 + li * 100 + a // chunk, dev, torch.bfloat16)
             v = device_normal((1, chunk, Hkv, D), 9000 + li * 100 + a // chunk, dev, torch.bfloat16)
@@ -63,60 +113,167 @@ def bench_decode(args, dev):
     kn = device_normal((total, 1, 1, Hkv, D), 12, dev, torch.bfloat16)
     vn = device_normal((total, 1, 1, Hkv, D), 13, dev, torch.bfloat16)
     out = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    W = w.sink + w.recent
     torch.cuda.synchronize()
     for s in range(args.warmup):
         layers[s % L].decode(q[s], kn[s], vn[s], out)
     torch.cuda.synchronize()
-    # timed region 1: the plain step loop (value, ms_per_step)
-    steps_a = args.steps // 2
-    steps_b = args.steps - steps_a
-    nbytes_a = 0
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    n_before = [lay.n_tokens for lay in layers]
+    nbytes = 0
+    for i in range(args.steps):
+        li = (args.warmup + i) % L
+        nbytes += decode_step_bytes(n_before[li] + i // L, Hr, Hs, Hq, Hkv, D, W, D * 2 * 2)
+    t0, t1 = _events(torch)
     t0.record()
-    for i in range(steps_a):
+    for i in range(args.steps):
         s = args.warmup + i
-        lay = layers[s % L]
-        nbytes_a += _decode_step_bytes(lay.n_tokens, Hr, Hs, Hq, Hkv, D, w.sink + w.recent)
-        lay.decode(q[s], kn[s], vn[s], out)
+        layers[s % L].decode(q[s], kn[s], vn[s], out)
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    # timed region 2: HIP events around every launch of the decode kernel on
-    # the stream it runs on (average launch duration for the roofline)
-    nbytes_b = 0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps_b)]
-    for i in range(steps_b):
-        s = args.warmup + steps_a + i
-        lay = layers[s % L]
-        nbytes_b += _decode_step_bytes(lay.n_tokens, Hr, Hs, Hq, Hkv, D, w.sink + w.recent)
-        ev[i][0].record()
-        lay.decode(q[s], kn[s], vn[s], out)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_kern_ms = sum(kern_ms) / len(kern_ms)
-    ms_step = total_ms / steps_a
-    gbs = nbytes_a / (total_ms * 1e-3) / 1e9
-    achieved = (nbytes_b / steps_b) / (avg_kern_ms * 1e-3) / 1e9
-    nbytes = nbytes_a
-    res = {
+    ms = t0.elapsed_time(t1)
+    ms_step = ms / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # a step is exactly one launch of the decode kernel on the caller's stream,
+    # so the events above bracket `steps` back-to-back launches of it
+    return {
         "value": gbs, "ms_per_step": ms_step, "tok_per_s": 1000.0 / ms_step,
-        "bytes_per_step": nbytes / steps_a,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_kernel<128,1,bf16>",
-                     "avg_launch_us": avg_kern_ms * 1e3},
-        "layers_cycled": L,
+        "bytes_per_step": nbytes / args.steps, "layers_cycled": L,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "duo::decode_kernel<128, 1, duo::Bf16Tag>",
+                     "avg_launch_us": ms_step * 1e3},
     }
-    return res
+
+
+def bench_mha8(args, dev):
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+    w = WORKLOADS["mha8_d64_seq1024"]
+    H, D, T, steps = 8, 64, 1024, 16
+    q = device_normal((1, T, H, D), 21, dev, torch.bfloat16)
+    k = device_normal((1, T, H, D), 22, dev, torch.bfloat16)
+    v = device_normal((1, T, H, D), 23, dev, torch.bfloat16)
+    qs = device_normal((steps, 1, 1, H, D), 24, dev, torch.bfloat16)
+    ks = device_normal((steps, 1, 1, H, D), 25, dev, torch.bfloat16)
+    vs = device_normal((steps, 1, 1, H, D), 26, dev, torch.bfloat16)
+    out = torch.empty_like(q)
+    o1 = torch.empty((1, 1, H, D), dtype=torch.bfloat16, device=dev)
+    layers = [duo.DuoLayer(n_q_heads=H, n_kv_heads=H, head_dim=D, n_retrieval_kv_heads=2,
+                           capacity=T + steps, softmax_scale=w.softmax_scale, device=dev)
+              for _ in range(6)]
+
+    def run(lay):
+        lay.prefill_chunk(q, k, v, out)
+        for s in range(steps):
+            lay.decode(qs[s], ks[s], vs[s], o1)
+
+    run(layers[0])
+    times = sorted(time_region(torch, lambda lay=lay: run(lay)) for lay in layers[1:])
+    flops = (2 * causal_pairs(0, T) + 6 * lambda_pairs(0, T, 16, 64)) * 4 * D
+    return {"ms_prefill_1024_plus_16_decode": times[len(times) // 2],
+            "prefill_gflop": flops / 1e9}
+
+
+def bench_prefill_llama3(args, dev):
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+    w = WORKLOADS["llama3_8b_prefill_64k"]
+    Hq, Hkv, D, Hr = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_retrieval_kv
+    T, C = w.prefill_tokens, w.chunk
+    qc = [device_normal((1, C, Hq, D), 310 + i, dev, torch.bfloat16) for i in range(T // C)]
+    kc = [device_normal((1, C, Hkv, D), 320 + i, dev, torch.bfloat16) for i in range(T // C)]
+    vc = [device_normal((1, C, Hkv, D), 330 + i, dev, torch.bfloat16) for i in range(T // C)]
+    oc = [torch.empty_like(x) for x in qc]
+
+    def one_pass():
+        lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
+                           capacity=T, softmax_scale=w.softmax_scale, device=dev)
+        torch.cuda.synchronize()
+        a, b = _events(torch)
+        a.record()
+        for i in range(len(qc)):
+            lay.prefill_chunk(qc[i], kc[i], vc[i], oc[i])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    one_pass()
+    times = sorted(one_pass() for _ in range(args.prefill_reps))
+    ms = times[len(times) // 2]
+    G = Hq // Hkv
+    ret_flops = Hr * G * causal_pairs(0, T) * 4 * D
+    str_flops = (Hkv - Hr) * G * lambda_pairs(0, T, w.sink, w.recent) * 4 * D
+    return {"ms_full_prefill_8x8192": ms,
+            "tflops_total": (ret_flops + str_flops) / (ms * 1e-3) / 1e12,
+            "retrieval_tflop": ret_flops / 1e12, "streaming_tflop": str_flops / 1e12,
+            "mfma_frac_total": (ret_flops + str_flops) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
+def bench_mixed(args, dev):
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+    w = WORKLOADS["llama2_7b_mixed_16k"]
+    H, D, T = w.n_q_heads, w.head_dim, w.mixed_tokens
+    q = device_normal((1, T, H, D), 41, dev, torch.bfloat16)
+    k = device_normal((1, T, H, D), 42, dev, torch.bfloat16)
+    v = device_normal((1, T, H, D), 43, dev, torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(44)
+    alpha = torch.rand((H,), generator=g, device=dev, dtype=torch.float32)
+    out = torch.empty_like(q)
+    fn = lambda: duo.mixed_forward(q, k, v, alpha, softmax_scale=w.softmax_scale, out=out)
+    fn()
+    ms = sorted(time_region(torch, fn) for _ in range(5))[2]
+    flops = H * (causal_pairs(0, T) + lambda_pairs(0, T, w.sink, w.recent)) * 4 * D
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tflop": flops / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
+def bench_int4_decode(args, dev):
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+    w = WORKLOADS["llama3_8b_int4_decode_1m"]
+    Hq, Hkv, D, Hr = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_retrieval_kv
+    Hs = Hkv - Hr
+    N, steps, warm = w.context, args.int4_steps, 4
+    lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
+                       capacity=N + steps + warm, softmax_scale=w.softmax_scale, kv_dtype="fp16",
+                       retrieval_dtype="int4", device=dev)
+    chunk = 65536
+    for a in range(0, N, chunk):
+        kk = device_normal((1, chunk, Hkv, D), 5000 + a // chunk, dev, torch.float16)
+        vv = device_normal((1, chunk, Hkv, D), 6000 + a // chunk, dev, torch.float16)
+        lay.append_kv(kk, vv)
+    total = steps + warm
+    q = device_normal((total, 1, 1, Hq, D), 51, dev, torch.bfloat16)
+    kn = device_normal((total, 1, 1, Hkv, D), 52, dev, torch.float16)
+    vn = device_normal((total, 1, 1, Hkv, D), 53, dev, torch.float16)
+    out = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    for s in range(warm):
+        lay.decode(q[s], kn[s], vn[s], out)
+    torch.cuda.synchronize()
+    n0 = lay.n_tokens
+    nbytes = sum(decode_step_bytes(n0 + i, Hr, Hs, Hq, Hkv, D, w.sink + w.recent, 160)
+                 for i in range(steps))
+    t0, t1 = _events(torch)
+    t0.record()
+    for i in range(steps):
+        lay.decode(q[warm + i], kn[warm + i], vn[warm + i], out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_step": ms / steps, "tok_per_s": 1000.0 * steps / ms, "kv_gbs": gbs,
+            "bytes_per_step": nbytes / steps, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
 def cpu_baseline_decode(budget_s: float):
     """The oracle's decode step timed on the host: the Llama-2-7B layer at a
     32768-token context, repeated until `budget_s` seconds have elapsed."""
-    import numpy as np
     import oracle
     from duo_synth import WORKLOADS, make_inputs
     w = WORKLOADS["llama2_7b_decode_32k"]
@@ -124,14 +281,15 @@ def cpu_baseline_decode(budget_s: float):
     orc = oracle.OracleLayer(w.n_q_heads, w.n_kv_heads, w.head_dim, inp.retrieval_mask,
                              w.softmax_scale, w.sink, w.recent)
     orc.append(inp.k, inp.v)
+    Hr = w.n_retrieval_kv
     nbytes = 0
     t0 = time.perf_counter()
     steps = 0
     while steps < 64:
         n = orc.n
         orc.decode(inp.q_steps[steps], inp.k_steps[steps], inp.v_steps[steps])
-        nbytes += _decode_step_bytes(n, w.n_retrieval_kv, w.n_kv_heads - w.n_retrieval_kv,
-                                     w.n_q_heads, w.n_kv_heads, w.head_dim, w.sink + w.recent)
+        nbytes += decode_step_bytes(n, Hr, w.n_kv_heads - Hr, w.n_q_heads, w.n_kv_heads,
+                                    w.head_dim, w.sink + w.recent, w.head_dim * 4)
         steps += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -140,10 +298,10 @@ def cpu_baseline_decode(budget_s: float):
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        cores = os.cpu_count() or 1
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} oracle decode steps of the 32x128 layer at 32768 context "
-                      f"({dt:.1f} s)"}
+            "sample": f"{steps} oracle decode steps of the 32x128 layer at a 32768-token "
+                      f"context ({dt:.1f} s; float64 NumPy, BLAS threads = cores)"}
 
 
 def main():
@@ -152,8 +310,11 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--int4-steps", type=int, default=64)
+    ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of: decode,mha8,prefill,mixed,int4")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build",
@@ -161,18 +322,34 @@ def main():
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")
-    r = bench_decode(args, dev)
+    only = set(x for x in args.only.split(",") if x)
+    want = lambda name: not only or name in only
     line = {
         "metric": "duo-attn decode KV GB/s & tok/s; chunked-prefill TFLOP/s, Llama-3-8B layer",
-        "value": r["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "llama2_7b_decode_32k", "heads": "32x128 MHA, 8 retrieval",
-                   "context": 32768, "layers_cycled": r["layers_cycled"]},
-        "tok_per_s": r["tok_per_s"],
-        "roofline": r["roofline"],
+                   "context": 32768, "layers_cycled": args.layers},
     }
-    if not args.no_cpu_baseline:
+    work = {}
+    if want("decode"):
+        r = bench_decode_llama2(args, dev)
+        line["value"] = r["value"]
+        line["ms_per_step"] = r["ms_per_step"]
+        line["tok_per_s"] = r["tok_per_s"]
+        line["roofline"] = r["roofline"]
+        print(f"# decode llama2 32k: {r['value']:.0f} GB/s, {r['ms_per_step']*1e3:.1f} us/step",
+              file=sys.stderr, flush=True)
+    for name, key, fn in (("mha8", "mha8_d64_seq1024", bench_mha8),
+                          ("prefill", "llama3_8b_prefill_64k", bench_prefill_llama3),
+                          ("mixed", "llama2_7b_mixed_16k", bench_mixed),
+                          ("int4", "llama3_8b_int4_decode_1m", bench_int4_decode)):
+        if want(name):
+            work[key] = fn(args, dev)
+            print(f"# {key}: {json.dumps(work[key])}", file=sys.stderr, flush=True)
+    line["workloads"] = work
+    if want("decode") and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget)
     print(json.dumps(line), flush=True)
 
