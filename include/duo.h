@@ -78,7 +78,7 @@ typedef struct {
   int64_t retrieval_capacity;   /* max tokens held by the retrieval cache */
   duo_dtype kv_dtype;           /* dtype of k/v inputs and of the ring: BF16 | FP16 */
   duo_dtype retrieval_dtype;    /* kv_dtype, or INT4_G32 (then Hq/Hkv * D/32 <= 16) */
-  float softmax_scale;          /* multiplies q.k before the softmax */
+  float softmax_scale;          /* multiplies q.k before the softmax; finite, > 0 */
 } duo_layer_desc;
 
 /* Byte offsets of the arrays inside the caller-provided buffers.

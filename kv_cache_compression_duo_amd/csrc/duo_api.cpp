@@ -54,7 +54,7 @@ static duo_status check_desc(const duo_layer_desc* d) {
   if (d->kv_dtype != DUO_BF16 && d->kv_dtype != DUO_FP16) return DUO_ERR_UNSUPPORTED;
   if (d->retrieval_dtype != d->kv_dtype && d->retrieval_dtype != DUO_INT4_G32)
     return DUO_ERR_UNSUPPORTED;
-  if (!isfinite(d->softmax_scale)) return DUO_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return DUO_ERR_INVALID_ARG;
   // the 4-bit decode kernel maps (query head, channel group) pairs of a KV
   // head onto the 16 columns of one MFMA tile
   if (d->retrieval_dtype == DUO_INT4_G32 && G * (d->head_dim / 32) > 16) return DUO_ERR_UNSUPPORTED;

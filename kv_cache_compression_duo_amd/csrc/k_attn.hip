@@ -26,8 +26,8 @@
 //     B operand of the PV product (keys permuted inside each 16-key slice,
 //     which a sum over keys does not see);
 //   * K tiles are stored row-major in LDS (rows padded by 16 bytes), V tiles
-//     transposed (d-major, 8-byte key chunks XOR-swizzled by d) so that both
-//     MFMA operands are read with ds_read_b128 / ds_read_b64;
+//     transposed (d-major) with 4-key chunks paired and XOR-swizzled by d, so
+//     that both MFMA operands are read with one ds_read_b128 each;
 //   * the next tile's global loads are in flight while the current tile is
 //     computed; query tiles are launched longest-first (causal imbalance).
 #include "device_common.hpp"
@@ -62,6 +62,17 @@ constexpr int kBN = 64;  // keys per tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Position (in 8-byte units) of the 4-key chunk c of V^T row d in LDS. Chunks
+// are stored in pairs {4s + j, 4s + j + 2} (j = 0, 1), the two chunks one lane
+// of the PV product reads, so they come back in one ds_read_b128; pair slots
+// are XOR-swizzled by d so that 8 consecutive rows hit distinct banks.
+__device__ __forceinline__ int vt_slot(int c, int d) {
+  const int s4 = c >> 2, j = c & 3;              // c = 4*s4 + j
+  const int pair = 2 * s4 + (j & 1);            // {4s+0, 4s+2} -> 2s, {4s+1, 4s+3} -> 2s+1
+  const int half = j >> 1;                      // first or second chunk of the pair
+  return (((pair ^ (d & 7)) << 1) | half);
 }
 
 template <int D>
@@ -121,6 +132,10 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
   const int i_q = a.n + t_q;                          // and its position
   const int blk_last = (tok0 + BMT < a.T ? tok0 + BMT : a.T) - 1;
   const int i_min = a.n + tok0, i_max = a.n + blk_last;
+  // this wave's query positions (wave-uniform)
+  const int w_tok0 = tok0 + (wave / HB) * TOKW;
+  const int i_wfirst = a.n + w_tok0;
+  const int i_wlast = a.n + (w_tok0 + TOKW - 1 < a.T ? w_tok0 + TOKW - 1 : a.T - 1);
 
   // ---- key tiles visited by this block --------------------------------------
   int n1, w0, ntiles;
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
         uint32_t lo = __builtin_amdgcn_perm(word_of(vreg[1], i >> 1), word_of(vreg[0], i >> 1), sel);
         uint32_t hi = __builtin_amdgcn_perm(word_of(vreg[3], i >> 1), word_of(vreg[2], i >> 1), sel);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + d * kBN + 4 * (vg ^ (d & 15)));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + d * kBN + 4 * vt_slot(vg, d));
         dst[0] = lo;
         dst[1] = hi;
       }
@@ -190,8 +205,12 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
     for (int db = 0; db < DB; ++db) o_l[db] = f32x16{};
   }
 
-  // one online-softmax update of (m, l, O) from masked log2-domain scores;
-  // returns P packed as the B operands of the four 16-key slices
+  // One online-softmax update of (m, l, O) from masked raw scores (m in raw
+  // score units; the scale, folded with log2(e), enters the exp2 argument as
+  // one FMA). O and l are rescaled only when some lane's maximum grew
+  // (wave-uniform test); returns P packed as the B operands of the four
+  // 16-key slices.
+  const float c2 = a.scale_log2;
   auto softmax_update = [&](const float (&sc)[2][16], float& m, float& l, f32x16 (&O)[DB],
                             bf16x8 (&pb)[4]) {
     float tm = -INFINITY;
@@ -201,21 +220,24 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sc[kb][j]);
     tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
     const float mn = fmaxf(m, tm);
-    const float ms = mn == -INFINITY ? 0.0f : mn;  // no allowed key yet
-    const float corr = fast_exp2(m - ms);
-    m = mn;
+    if (__ballot(mn > m) != 0) {
+      const float corr = fast_exp2((m - mn) * c2);  // m = -inf -> 0 (mn is finite here)
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) O[db] *= corr;
+      m = mn;
+    }
+    const float mc = m == -INFINITY ? 0.0f : m * c2;  // no allowed key yet: p = 0
     float ls = 0.0f;
     float p[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        p[kb][j] = fast_exp2(sc[kb][j] - ms);
+        p[kb][j] = fast_exp2(fmaf(sc[kb][j], c2, -mc));
         ls += p[kb][j];
       }
-    l = l * corr + ls;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) O[db] *= corr;
+    l += ls;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -224,16 +246,16 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
   auto pv = [&](const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      bf16x8 av[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
         const int d = 32 * db + q32;
-        const int sw = d & 15;
-        const uint16_t* row = Vt + d * kBN;
-        const uint2 x = *reinterpret_cast<const uint2*>(row + 4 * ((4 * s + h2) ^ sw));
-        const uint2 y = *reinterpret_cast<const uint2*>(row + 4 * ((4 * s + 2 + h2) ^ sw));
-        const bf16x8 av = as_bf16x8(u32x4{x.x, x.y, y.x, y.y});
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[s], O[db], 0, 0, 0);
+        av[db] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + d * kBN + 4 * vt_slot(4 * s + h2, d)));
       }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], pb[s], O[db], 0, 0, 0);
     }
   };
 
@@ -252,39 +274,53 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
     for (int kb = 0; kb < 2; ++kb) {
       st[kb] = f32x16{};
       const uint16_t* krow = Ks + (32 * kb + q32) * KPAD + 8 * h2;
+      bf16x8 ak[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], st[kb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qf[ks], st[kb], 0, 0, 0);
     }
-    // scores in the log2 domain with this mode's mask
-    float sf[2][16];
-    float sl[2][16];
+    // raw scores with this mode's mask; tiles wholly below the wave's first
+    // query need no causal mask, tiles wholly above its last query are skipped
+    const bool live = p0 <= i_wlast;
+    const bool diag = p0 + kBN - 1 > i_wfirst;
     const bool lam_tile = kMixed && (p0 < a.S || p0 + kBN - 1 >= i_min - a.R + 1);
+    if (live) {
+      float sf[2][16];
+      float sl[2][16];
+      if (MODE == MODE_STREAMING || diag || kMixed) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
-        const float x = st[kb][j] * a.scale_log2;
-        const bool causal = jp <= i_q;
-        const bool lam = causal && (jp < a.S || i_q - jp < a.R);
-        if constexpr (MODE == MODE_STREAMING) {
-          sf[kb][j] = lam ? x : -INFINITY;
-        } else {
-          sf[kb][j] = causal ? x : -INFINITY;
-          if constexpr (kMixed) sl[kb][j] = lam ? x : -INFINITY;
-        }
+          for (int j = 0; j < 16; ++j) {
+            const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
+            const float x = st[kb][j];
+            const bool causal = jp <= i_q;
+            const bool lam = causal && (jp < a.S || i_q - jp < a.R);
+            if constexpr (MODE == MODE_STREAMING) {
+              sf[kb][j] = lam ? x : -INFINITY;
+            } else {
+              sf[kb][j] = causal ? x : -INFINITY;
+              if constexpr (kMixed) sl[kb][j] = lam ? x : -INFINITY;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sf[kb][j] = st[kb][j];
       }
-    bf16x8 pb[4];
-    softmax_update(sf, m_f, l_f, o_f, pb);
-    pv(pb, o_f);
-    if constexpr (kMixed) {
-      if (lam_tile) {
-        bf16x8 pl[4];
-        softmax_update(sl, m_l, l_l, o_l, pl);
-        pv(pl, o_l);
+      bf16x8 pb[4];
+      softmax_update(sf, m_f, l_f, o_f, pb);
+      pv(pb, o_f);
+      if constexpr (kMixed) {
+        if (lam_tile) {
+          bf16x8 pl[4];
+          softmax_update(sl, m_l, l_l, o_l, pl);
+          pv(pl, o_l);
+        }
       }
     }
     __syncthreads();  // every wave is done with this tile's LDS

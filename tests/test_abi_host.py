@@ -64,6 +64,8 @@ def test_layout_sizes():
     (dict(capacity=-5), 1),
     (dict(kv_dtype="bf16", retrieval_dtype="fp16"), 2),
     (dict(softmax_scale=float("inf")), 1),
+    (dict(softmax_scale=0.0), 1),
+    (dict(softmax_scale=-0.1), 1),
 ])
 def test_bad_descriptor_rejected(kw, status):
     L = _lib()
