@@ -23,51 +23,43 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 }
 
 // ml: [G][max_split][2], acc: [G][max_split][D]; out row g at out + g*D (bf16).
-// One pass: thread (part, d) folds the splits part, part+P, ... into a running
-// (m, l, o) with independent loads (no dependent round trips through LDS),
-// then the P parts of each channel are folded through LDS.
+// Thread (part, d) folds the splits part, part + P, ... into a running
+// (m, l, o). Loads are issued UN splits at a time with clamped (always valid)
+// addresses, so a batch costs one memory round trip; entries past the last
+// split get weight 0. The P parts of each channel are then folded in LDS.
 template <int D, int G>
 __device__ void merge_splits(MergeLds& s, const float* __restrict__ ml,
                              const float* __restrict__ acc, int max_split, int n_split,
                              uint16_t* __restrict__ out) {
   constexpr int P = kMergeThreads / D;  // threads per output channel
-  constexpr int UN = 4;
+  constexpr int UN = 16;
   const int t = threadIdx.x;
   const int d = t % D, part = t / D;
   for (int g = 0; g < G; ++g) {
     const float* mlg = ml + (int64_t)g * max_split * 2;
     const float* ag = acc + (int64_t)g * max_split * D + d;
     float m = -INFINITY, l = 0.0f, o = 0.0f;
-    int sp = part;
-    for (; sp + (UN - 1) * P < n_split; sp += UN * P) {
+    for (int sp0 = part; sp0 < n_split; sp0 += UN * P) {
       float mm[UN], ll[UN], aa[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        mm[u] = ld_agent(mlg + (sp + u * P) * 2);
-        ll[u] = ld_agent(mlg + (sp + u * P) * 2 + 1);
-        aa[u] = ld_agent(ag + (int64_t)(sp + u * P) * D);
+        const int sp = sp0 + u * P < n_split ? sp0 + u * P : n_split - 1;
+        mm[u] = ld_agent(mlg + sp * 2);
+        ll[u] = ld_agent(mlg + sp * 2 + 1);
+        aa[u] = ld_agent(ag + (int64_t)sp * D);
       }
       float mx = m;
 #pragma unroll
       for (int u = 0; u < UN; ++u) mx = fmaxf(mx, mm[u]);
-      const float c = fast_exp2(m - mx);
+      const float c = fast_exp2(m - mx);  // m = -inf on the first batch -> 0
       l *= c;
       o *= c;
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const float w = fast_exp2(mm[u] - mx);
+        const float w = sp0 + u * P < n_split ? fast_exp2(mm[u] - mx) : 0.0f;
         l = fmaf(ll[u], w, l);
         o = fmaf(aa[u], w, o);
       }
-      m = mx;
-    }
-    for (; sp < n_split; sp += P) {
-      const float mi = ld_agent(mlg + sp * 2), li = ld_agent(mlg + sp * 2 + 1);
-      const float ai = ld_agent(ag + (int64_t)sp * D);
-      const float mx = fmaxf(m, mi);
-      const float c = fast_exp2(m - mx), w = fast_exp2(mi - mx);
-      l = l * c + li * w;
-      o = o * c + ai * w;
       m = mx;
     }
     s.part[t] = m;
