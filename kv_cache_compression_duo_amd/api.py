@@ -133,14 +133,16 @@ class DuoLayer:
 
     def retrieval_int4(self):
         """Views of a 4-bit retrieval cache (cap32 = capacity rounded up to 32):
-        K codes [B,Hr,cap32,D/2] u8 (token-major), V codes
-        [B,Hr,cap32/32,D,16] u8 (32-token blocks, byte m of a channel row =
-        token m | token m+16 << 4), K and V scale/zero [B,Hr,cap32,D/32,2] fp16."""
+        K codes [B,Hr,cap32,D/2] u8 (token-major, byte b = channel 2b | 2b+1 << 4),
+        V codes [B,Hr,cap32/32,16*D] u8 (32-token blocks; channel ch, tokens m
+        (low nibble) and m+16 (high nibble) of a block sit at byte
+        16*(4*(16*(ch//64) + ch%16) + m//4) + 4*((ch%64)//16) + m%4), K and V
+        scale/zero [B,Hr,cap32/32,D/32,32,2] fp16 (block, group, token in block)."""
         assert self.retrieval_dtype == "int4"
         cap32 = (self.capacity + 31) // 32 * 32
         ks = (self.B, self.Hr, cap32, self.D // 2)
-        vs = (self.B, self.Hr, cap32 // 32, self.D, 16)
-        ss = (self.B, self.Hr, cap32, self.D // 32, 2)
+        vs = (self.B, self.Hr, cap32 // 32, 16 * self.D)
+        ss = (self.B, self.Hr, cap32 // 32, self.D // 32, 32, 2)
         return (_bytes_view(self.rbuf, self.layout.k_offset, ks, torch.uint8),
                 _bytes_view(self.rbuf, self.layout.v_offset, vs, torch.uint8),
                 _bytes_view(self.rbuf, self.layout.k_sz_offset, ss, torch.float16),

@@ -41,6 +41,9 @@ def common_flags():
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         # packed FP32 VALU forms are kept out of every kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators live in ordinary VGPRs (no AGPR copies
+        # around VALU updates of an accumulator)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"),
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     ]

@@ -28,7 +28,7 @@ __device__ __forceinline__ void attend_rows(WaveState<G>& st, const float (&qf)[
   constexpr int RPL = 64 / LPR;    // rows per load
   constexpr int U = kTile / RPL;   // loads per tile
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lc = lane % LPR, lr = lane / LPR;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -145,7 +145,7 @@ template <int D, int G>
 __device__ __forceinline__ void block_merge(BlockRed<D, G>& red, const WaveState<G>& st) {
   constexpr int LPR = D / 8;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {

@@ -3,6 +3,7 @@
 // a failed call enqueues nothing and leaves the layer unchanged.
 #include <math.h>
 #include <new>
+#include <stdlib.h>
 #include <string.h>
 
 #include "duo_internal.hpp"
@@ -15,6 +16,31 @@ int max_split_for(const duo_layer_desc& d) {
   int64_t cap = d.retrieval_capacity;
   int64_t s = (cap + kMinSplitTokens - 1) / kMinSplitTokens + 1;
   return (int)(s < 1 ? 1 : s);
+}
+
+// About one retrieval split per compute unit: a streaming read of the cache
+// runs fastest with one 256-thread block per CU, and a CU that gets two
+// blocks while others get one sets the step time. Streaming-head blocks read
+// at most S + R rows, so four of them are counted as one block.
+// DUO_DECODE_SPLIT_TOKENS, if set to a positive value, overrides the rule.
+int decode_split_tokens(const duo_layer* L, int64_t rows, int tile) {
+  static int env = -1;
+  if (env < 0) {
+    const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
+    env = e ? atoi(e) : 0;
+    if (env < 0) env = 0;
+  }
+  int64_t st = env;
+  if (st <= 0) {
+    const int B = L->d.batch;
+    int64_t per_head = (int64_t)(L->cus - (B * L->Hs) / 4) / ((int64_t)B * (L->Hr > 0 ? L->Hr : 1));
+    if (per_head < 1) per_head = 1;
+    st = (rows + per_head - 1) / per_head;
+  }
+  st = (st + tile - 1) / tile * tile;
+  if (st < kMinSplitTokens) st = kMinSplitTokens;
+  if (st > (int64_t)1 << 30) st = (int64_t)1 << 30;
+  return (int)st;
 }
 
 size_t ws_bytes(const duo_layer_desc& d, int max_split) {
@@ -128,6 +154,12 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrie
   L->Hr = d->n_retrieval_kv_heads;
   L->Hs = d->n_kv_heads - d->n_retrieval_kv_heads;
   L->max_split = max_split_for(*d);
+  int dev = 0;
+  L->cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      L->cus <= 0)
+    L->cus = 256;
   if (launch_zero(workspace, lay.workspace_bytes, stream) != hipSuccess) {
     delete L;
     return DUO_ERR_HIP;

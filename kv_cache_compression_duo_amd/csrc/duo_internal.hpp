@@ -14,6 +14,7 @@ struct duo_layer {
   int64_t n;      // tokens cached
   int G, Hr, Hs;  // group size, retrieval / streaming KV heads
   int max_split;  // split-K partial slots per retrieval (batch, KV head)
+  int cus;        // compute units of the device the layer was attached on
 };
 
 namespace duo {
@@ -34,6 +35,9 @@ struct WsView {
 WsView ws_view(const duo_layer* L);
 size_t ws_bytes(const duo_layer_desc& d, int max_split);
 int max_split_for(const duo_layer_desc& d);
+// Split-K range (tokens, a multiple of `tile`, at least kMinSplitTokens) of a
+// decode step over `rows` cache rows.
+int decode_split_tokens(const duo_layer* L, int64_t rows, int tile);
 
 // ---- launchers (return hipSuccess or the launch error) ----------------------
 hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v, int T,

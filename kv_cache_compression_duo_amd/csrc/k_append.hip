@@ -72,13 +72,16 @@ __device__ __forceinline__ void encode_group_part(const u32x4& raw, uint32_t* co
 
 // 4-bit cache append. Key codes are token-major ([cap32][D/2] bytes, byte b of
 // a row = channel 2b | channel 2b+1 << 4). Value codes are stored in 32-token
-// blocks [cap32/32][D][16 bytes] where byte m of a channel row holds token m
-// of the block in its low nibble and token m + 16 in its high nibble (the
-// operand order of the decode kernel's PV product). A thread owns one byte
-// position m of a block (tokens m and m + 16) and 8 channels, so no two
-// threads write the same byte; a byte whose other token lies outside the
-// appended range is read, modified and written by its one owner. Scale and
-// zero-point words are [cap32][D/32] (fp16 s | fp16 z << 16).
+// blocks of 16*D bytes laid out in the operand order of the decode kernel's PV
+// product: for channel ch and m in [0, 16), the byte at
+//   16 * (4 * (16 * (ch / 64) + ch % 16) + m / 4) + 4 * ((ch % 64) / 16) + m % 4
+// holds token m of the block in its low nibble and token m + 16 in its high
+// nibble. Scale and zero-point words (fp16 s | fp16 z << 16) are blocked the
+// same way: [cap32/32][D/32][32], word t % 32 of group g of block t / 32.
+// A thread owns one byte position m of a block (tokens m and m + 16) and 8
+// channels, so no two threads write the same byte; a byte whose other token
+// lies outside the appended range is read, modified and written by its one
+// owner.
 // Thread order: channel chunk fastest, so the 4 lanes of a quad hold one
 // 32-channel group of one token (the min/max reduction uses quad DPP).
 template <typename Tag>
@@ -115,17 +118,20 @@ __global__ void append_int4_kernel(const u32x4* __restrict__ k, const u32x4* __r
       const int64_t row = hb * cap32 + p;
       kcodes[row * chunks + c] = kq;
       if ((c & 3) == 0) {
-        ksz[row * groups + c / 4] = ks;
-        vsz[row * groups + c / 4] = vs;
+        const int64_t w = ((hb * (cap32 / 32) + p / 32) * groups + c / 4) * 32 + p % 32;
+        ksz[w] = ks;
+        vsz[w] = vs;
       }
     }
   }
   if (!in[0] && !in[1]) return;  // this byte pair lies outside the appended range
-  // value codes: channel rows 8c .. 8c+7 of block blk, byte m
-  uint8_t* vb = vcodes + ((hb * (cap32 / 32) + blk) * D + 8 * c) * 16 + m;
+  // value codes of channels ch = 8c + j, j < 8: the bytes for consecutive j
+  // are 64 apart (ch % 16 steps by one)
+  uint8_t* vb = vcodes + (hb * (cap32 / 32) + blk) * 16 * D +
+                16 * (4 * (16 * (c / 8) + 8 * (c % 2)) + m / 4) + 4 * ((c % 8) / 2) + m % 4;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint8_t* dst = vb + 16 * j;
+    uint8_t* dst = vb + 64 * j;
     const uint32_t lo = (vq[0] >> (4 * j)) & 0xFu, hi = (vq[1] >> (4 * j)) & 0xFu;
     uint32_t byte;
     if (in[0] && in[1]) {

@@ -18,12 +18,9 @@
 // the G query heads of a KV head share every K/V load. Scores are reduced
 // across the lanes of a row with DPP; only the tile maximum crosses rows.
 // Blocks [0, Hs) are streaming heads, the next Hr*n_split blocks are
-// retrieval splits, sized so that the grid fills the resident block slots of
-// the chip once. The new token is read from the input (never from the
+// retrieval splits, sized to about one block per compute unit. The new token is read from the input (never from the
 // cache) in this launch, and written to its cache row / ring slot by one
 // block, so no block reads memory another block writes.
-#include <stdlib.h>
-
 #include "device_common.hpp"
 #include "decode_common.hpp"
 #include "duo_internal.hpp"
@@ -153,46 +150,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-static int env_split_tokens() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
-    v = e ? atoi(e) : 0;
-    if (v < 0) v = 0;
-  }
-  return v;
-}
-
-// Resident 256-thread blocks of a kernel on the current device (all CUs).
-template <typename K>
-static int resident_blocks(K kernel) {
-  int dev = 0, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess ||
-      cus <= 0 || per <= 0)
-    return 512;
-  return cus * per;
-}
-
-// Split size: the Hr*B*n_split retrieval blocks plus the Hs*B streaming
-// blocks fill the resident slots once (equal-sized splits finish together);
-// splits are whole 32-row tiles and at least kMinSplitTokens rows.
 template <int D, int G, typename Tag>
-static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int max_split, hipStream_t s) {
-  int st = env_split_tokens();
-  if (st <= 0 && a.Hr > 0) {
-    static int resident = 0;  // per kernel instance
-    if (!resident) resident = resident_blocks(decode_kernel<D, G, Tag>);
-    int slots = resident / B - a.Hs;
-    int per_head = slots / a.Hr;
-    if (per_head < 1) per_head = 1;
-    int64_t t = (rows + per_head - 1) / per_head;
-    st = (int)((t + kTile - 1) / kTile * kTile);
-  }
-  if (st < kMinSplitTokens) st = kMinSplitTokens;
-  a.split_tokens = st;
-  a.n_split = a.Hr > 0 ? (int)((rows + st - 1) / st) : 0;
+static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int split_tokens, int max_split,
+                           hipStream_t s) {
+  a.split_tokens = split_tokens;
+  a.n_split = a.Hr > 0 ? (int)((rows + split_tokens - 1) / split_tokens) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
   decode_kernel<D, G, Tag><<<grid, 256, 0, s>>>(a);
@@ -200,13 +162,13 @@ static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int max_split, hip
 }
 
 template <int D, typename Tag>
-static hipError_t launch_g(int G, const DecodeArgs& a, int B, int64_t rows, int max_split,
-                           hipStream_t s) {
+static hipError_t launch_g(int G, const DecodeArgs& a, int B, int64_t rows, int st,
+                           int max_split, hipStream_t s) {
   switch (G) {
-    case 1: return launch_t<D, 1, Tag>(a, B, rows, max_split, s);
-    case 2: return launch_t<D, 2, Tag>(a, B, rows, max_split, s);
-    case 4: return launch_t<D, 4, Tag>(a, B, rows, max_split, s);
-    default: return launch_t<D, 8, Tag>(a, B, rows, max_split, s);
+    case 1: return launch_t<D, 1, Tag>(a, B, rows, st, max_split, s);
+    case 2: return launch_t<D, 2, Tag>(a, B, rows, st, max_split, s);
+    case 4: return launch_t<D, 4, Tag>(a, B, rows, st, max_split, s);
+    default: return launch_t<D, 8, Tag>(a, B, rows, st, max_split, s);
   }
 }
 
@@ -238,12 +200,14 @@ hipError_t launch_decode(const duo_layer* L, const void* q, const void* k_new,
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;
   const int B = d.batch;
+  const int st = decode_split_tokens(L, rows, kTile);
+  const int ms = L->max_split;
   if (d.head_dim == 128) {
-    if (d.kv_dtype == DUO_FP16) return launch_g<128, Fp16Tag>(L->G, a, B, rows, L->max_split, s);
-    return launch_g<128, Bf16Tag>(L->G, a, B, rows, L->max_split, s);
+    if (d.kv_dtype == DUO_FP16) return launch_g<128, Fp16Tag>(L->G, a, B, rows, st, ms, s);
+    return launch_g<128, Bf16Tag>(L->G, a, B, rows, st, ms, s);
   }
-  if (d.kv_dtype == DUO_FP16) return launch_g<64, Fp16Tag>(L->G, a, B, rows, L->max_split, s);
-  return launch_g<64, Bf16Tag>(L->G, a, B, rows, L->max_split, s);
+  if (d.kv_dtype == DUO_FP16) return launch_g<64, Fp16Tag>(L->G, a, B, rows, st, ms, s);
+  return launch_g<64, Bf16Tag>(L->G, a, B, rows, st, ms, s);
 }
 
 }  // namespace duo

@@ -12,29 +12,32 @@
 // Exact refactoring used here (no dequantised tensor is formed):
 //   q . k^_t = sum_g [ s_tg * sum_{d in g} q_d c_td  +  z_tg * sum_{d in g} q_d ]
 //   sum_t p_t v^_td = sum_t (p_t s_tg) c_td + sum_t p_t z_tg        (g = g(d))
-// Key codes enter the QK MFMA as bf16 128 + c (exact, one v_perm per pair)
-// and the offset is removed from the per-group dot afterwards. Value codes
-// enter the PV MFMA as exact fp16 c ((1024 + c) - 1024 with packed fp16 adds),
-// so the rounded p * s_V operand (fp16, 11-bit significand) appears in no
-// other term and needs no matching correction. Q stays bf16 as given.
+// Key codes enter the QK MFMA as bf16 128 + c (exact, one v_perm per pair);
+// the accumulator starts at -128 * sum_{d in g} q_d, which removes the offset.
+// Value codes enter the PV MFMA as exact fp16 c ((1024 + c) - 1024 with packed
+// fp16 subtracts; the matrix cores do not keep fp16 subnormal operands exact,
+// so c * 2^-24 bit patterns are not used), so the rounded p * s_V operand
+// (fp16, 11-bit significand) appears in no other term and needs no matching
+// correction. Q stays bf16 as given.
 //
-// gfx950 design (v_mfma_f32_16x16x32_bf16, one wave = 32 tokens per tile):
-//   * QK: A = key codes (16 tokens x 32 channels of group g), B = a
-//     block-diagonal Q^T whose 16 columns are (query head h, group g') pairs,
-//     zero unless g' = g. Four MFMAs (one per group) fill all 16 columns with
-//     the per-group partial dots, so the scale/zero epilogue runs on every
-//     lane without padding waste; the groups are then summed with DPP;
+// gfx950 design (v_mfma_f32_16x16x32_bf16 / _f16, one wave = 32 tokens per
+// tile, the next tile's loads in flight while the current one is computed):
+//   * QK: A = key codes, rows = 16 tokens, k = the 8 channels a lane unpacks
+//     from one code word. A lane loads D/8 contiguous bytes of a token row
+//     (one 16-byte load for D = 128), i.e. all its channels lie in one
+//     32-channel group. B = a block-diagonal Q^T whose 16 columns are
+//     (query head h, group g) pairs, zero where the lane's channels are not in
+//     group g, so the accumulator column (h, g) collects the group-g partial
+//     dot; the groups are then summed with DPP and the scale/zero epilogue
+//     runs on every lane without padding waste;
 //   * PV (fp16 MFMA): A = p * s_V for the lane's (head, group) row and its 8
-//     tokens -- the
-//     very tokens and row the QK accumulator left in that lane, so no shuffle
-//     is needed -- and B = value codes. Value codes are stored transposed in
-//     32-token blocks, [channel][16 bytes], byte m holding tokens m (low
-//     nibble) and m + 16 (high nibble), which is exactly the B operand order;
-//   * key codes keep the token-major layout (byte b of a row: channel 2b low
-//     nibble, 2b + 1 high); the v_perm unpacking yields channels in the order
-//     0,2,4,6,1,3,5,7 of each 8-channel word and Q is loaded in that order.
-#include <stdlib.h>
-
+//     tokens -- the very tokens and row the QK accumulator left in that lane,
+//     so no shuffle is needed -- and B = value codes, whose block layout makes
+//     a lane's operands for 4 consecutive 16-channel n-blocks one 16-byte load;
+//   * the scale/zero words of the lane's group and tokens are contiguous in
+//     the blocked [block][group][32] layout: two 16-byte loads per tile each
+//     for K and V;
+//   * the running maximum is rescaled only when some lane's maximum grows.
 #include "decode_common.hpp"
 #include "duo_internal.hpp"
 #include "split_merge.hpp"
@@ -44,15 +47,16 @@ namespace duo {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Int4DecodeArgs {
   const uint16_t* q;       // [B][Hq][D] bf16
   const uint16_t* k_new;   // [B][Hkv][D] ring dtype
   const uint16_t* v_new;
   uint16_t* out;           // [B][Hq][D] bf16
-  const uint32_t* kcodes;  // [B][Hr][cap32][D/8] words
-  const uint32_t* vcodes;  // [B][Hr][cap32/32][D][4] words
-  const uint32_t* ksz;     // [B][Hr][cap32][D/32] (fp16 s | fp16 z << 16)
+  const uint8_t* kcodes;   // [B][Hr][cap32][D/2] bytes
+  const uint8_t* vcodes;   // [B][Hr][cap32/32][16 D] bytes
+  const uint32_t* ksz;     // [B][Hr][cap32/32][D/32][32] (fp16 s | fp16 z << 16)
   const uint32_t* vsz;
   uint16_t* kr;            // ring [B][Hs][S+R][D]
   uint16_t* vr;
@@ -66,14 +70,14 @@ struct Int4DecodeArgs {
   float qscale;            // softmax scale * log2(e)
 };
 
-// 8 nibbles -> 16-bit floats (OFF + c) with high byte HB (bf16 0x43.. = 128 + c,
-// fp16 0x64.. = 1024 + c, both exact), in the order low nibbles of bytes
-// 0..3, then high nibbles.
+// 8 nibbles of a word -> 8 16-bit lanes whose low byte is the code and high
+// byte is HB (bf16 0x43.. = 128 + c, fp16 0x64.. = 1024 + c, both exact), in
+// the order low nibbles of bytes 0..3, then high nibbles.
 template <uint32_t HB>
 __device__ __forceinline__ u32x4 nib8_to_16(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu;
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t cb = HB * 0x01010101u;
+  const uint32_t cb = HB * 0x01010101u;  // selector bytes 4..7 pick from cb
   u32x4 r;
   r.x = __builtin_amdgcn_perm(cb, lo, 0x04010400u);
   r.y = __builtin_amdgcn_perm(cb, lo, 0x04030402u);
@@ -92,11 +96,70 @@ __device__ __forceinline__ f16x8 nib8_to_f16(uint32_t w) {
   return biased - off;
 }
 
-__device__ __forceinline__ float h2f_lo(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// (scale, zero) of a packed word as floats
+__device__ __forceinline__ float sz_scale(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w).x;
 }
-__device__ __forceinline__ float h2f_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+__device__ __forceinline__ float sz_zero(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w).y;
+}
+
+// x *= c in the register that holds x. Written as one tied-operand
+// instruction so that the rarely taken rescale branch updates the
+// accumulators where they are, instead of the compiler copying all of them
+// on the path that skips it.
+__device__ __forceinline__ float scale_in_place(float x, float c) {
+  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(c));
+  return x;
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// One wave-tile of 32 tokens as a lane holds it.
+template <int D>
+struct I4Tile {
+  static constexpr int KW = D / 32;  // key code words per lane per 16 tokens
+  static constexpr int NC = D / 64;  // 16-byte value code loads per lane
+  uint32_t k[2][KW];
+  u32x4 v[NC];
+  u32x4 ks[2], vs[2];
+};
+
+// Offsets are 32-bit from per-head bases (the layout check bounds a head's
+// code and scale arrays below 2^31 bytes), so the loads take a uniform base.
+template <int D>
+__device__ __forceinline__ void load_tile(I4Tile<D>& T, const uint8_t* __restrict__ kc,
+                                          const uint8_t* __restrict__ vc,
+                                          const uint32_t* __restrict__ ks,
+                                          const uint32_t* __restrict__ vs, int t0, int n16,
+                                          int q4, int gc) {
+  constexpr int NG = D / 32;
+  const uint32_t t = (uint32_t)t0;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint8_t* p = kc + ((t + 16 * hf + n16) * (D / 2) + q4 * (D / 8));
+    if constexpr (D == 128) {
+      const u32x4 w = ld16_nt(p);
+      T.k[hf][0] = w.x; T.k[hf][1] = w.y; T.k[hf][2] = w.z; T.k[hf][3] = w.w;
+    } else {
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      T.k[hf][0] = w.x; T.k[hf][1] = w.y;
+    }
+  }
+  const uint32_t blk = t >> 5;
+#pragma unroll
+  for (int c4 = 0; c4 < I4Tile<D>::NC; ++c4)
+    T.v[c4] = ld16_nt(vc + (blk * 16 * D + ((c4 * 16 + n16) * 4 + q4) * 16));
+  const uint32_t sw = (blk * NG + gc) * 32 + 4 * q4;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    T.ks[hf] = ld16_nt(ks + (sw + 16 * hf));
+    T.vs[hf] = ld16_nt(vs + (sw + 16 * hf));
+  }
 }
 
 template <int D, int G, typename RingTag>
@@ -104,14 +167,14 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   constexpr int NG = D / 32;     // channel groups
   constexpr int NCOL = G * NG;   // used MFMA columns (head, group)
   constexpr int NB = D / 16;     // 16-channel n-blocks of the PV product
-  constexpr int W = D / 8;       // code words per token row
   static_assert(NCOL <= 16, "G * D / 32 must fit 16 MFMA columns");
   __shared__ BlockRed<D, G> red;
   __shared__ MergeLds mlds;
   __shared__ int is_last;
 
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const bool retrieval = (int)blockIdx.x >= a.Hs;
   const int rb = (int)blockIdx.x - a.Hs;
   const int kvh = retrieval ? rb / a.n_split : a.Hr + (int)blockIdx.x;
@@ -162,33 +225,41 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   const int n16 = lane & 15, q4 = lane >> 4;
   const int hc = n16 / NG, gc = n16 % NG;  // this lane's (head, group) column
   const bool col_ok = n16 < NCOL;
+  constexpr int KW = I4Tile<D>::KW;
+  // group of the channels this lane unpacks from a key row (D/4 per lane)
+  const int lane_group = q4 * D / 128;
 
-  // block-diagonal Q^T operands (one per group) and per-column q sums
-  bf16x8 qop[NG];
+  // block-diagonal Q^T operands (one per code word) and per-column q sums
+  bf16x8 qop[KW];
   float qsum;
   {
     const uint16_t* qh = a.q + ((int64_t)b * a.Hq + kvh * G + (col_ok ? hc : 0)) * D;
-    const u32x4 raw = ld16(qh + 32 * gc + 8 * q4);  // channels 32gc + 8q4 .. +7
-    constexpr int perm8[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    // sum of the column's group of Q (32 channels: 4 lanes x 8)
+    const u32x4 graw = ld16(qh + 32 * gc + 8 * q4);
     float s8 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s8 += __uint_as_float((uint32_t)half_of(raw, i) << 16);
+    for (int i = 0; i < 8; ++i) s8 += __uint_as_float((uint32_t)half_of(graw, i) << 16);
     s8 += __shfl_xor(s8, 16, 64);
     s8 += __shfl_xor(s8, 32, 64);
     qsum = col_ok ? s8 : 0.0f;
+    // B operand of code word j: channels q4*D/4 + 8j + {0,2,4,6,1,3,5,7}
+    constexpr int perm8[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    const bool diag = col_ok && lane_group == gc;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int j = 0; j < KW; ++j) {
+      const u32x4 raw = ld16(qh + q4 * (D / 4) + 8 * j);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint16_t bits = (col_ok && g == gc) ? half_of(raw, perm8[i]) : (uint16_t)0;
-        qop[g][i] = __builtin_bit_cast(__bf16, bits);
+        const uint16_t bits = diag ? half_of(raw, perm8[i]) : (uint16_t)0;
+        qop[j][i] = __builtin_bit_cast(__bf16, bits);
       }
     }
   }
-  const float qs128 = 128.0f * qsum;
+  const float qoff = -128.0f * qsum;
+  const float qscale = a.qscale;
 
-  const uint32_t* kc = a.kcodes + hb * a.cap32 * W;
-  const uint32_t* vc = a.vcodes + hb * a.cap32 * (D / 2) / 4;
+  const uint8_t* kc = a.kcodes + hb * a.cap32 * (D / 2);
+  const uint8_t* vc = a.vcodes + hb * a.cap32 * (D / 2);
   const uint32_t* ks = a.ksz + hb * a.cap32 * NG;
   const uint32_t* vs = a.vsz + hb * a.cap32 * NG;
 
@@ -197,90 +268,113 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = r0 + wave * 32; t0 < r1; t0 += kWaves * 32) {
-    // ---- loads (all inside the 32-token-aligned allocation) ----
-    uint32_t kw[2][NG], vw[NB], kszw[2][4], vszw[2][4];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-        kw[hf][g] = __builtin_nontemporal_load(kc + (int64_t)(t0 + 16 * hf + n16) * W + 4 * g + q4);
-    const uint32_t* vblk = vc + (int64_t)(t0 >> 5) * D * 4;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      vw[nb] = __builtin_nontemporal_load(vblk + (16 * nb + n16) * 4 + q4);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * hf + 4 * q4 + r;
-        kszw[hf][r] = ks[(int64_t)t * NG + gc];
-        vszw[hf][r] = vs[(int64_t)t * NG + gc];
-      }
+  // FULL: all 32 tokens of the tile are below r1 (no masking, no stale
+  // scale words); only the last tile of a split can be partial.
+  auto compute = [&](const I4Tile<D>& T, int t0, auto full_c) {
+    constexpr bool full = decltype(full_c)::value;
     // ---- scores: per-group dots on MFMA, scale/zero epilogue, group sum ----
     float sc[2][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      f32x4 pk = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 pk = f32x4{qoff, qoff, qoff, qoff};
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nib8_to_bf16(kw[hf][g]), qop[g], pk, 0, 0, 0);
+      for (int j = 0; j < KW; ++j)
+        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nib8_to_bf16(T.k[hf][j]), qop[j], pk, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float s = h2f_lo(kszw[hf][r]), z = h2f_hi(kszw[hf][r]);
-        float v = fmaf(s, pk[r] - qs128, z * qsum);
+        const uint32_t w = word_of(T.ks[hf], r);
+        float v = fmaf(sz_scale(w), pk[r], sz_zero(w) * qsum);
         if constexpr (NG >= 2) v += dpp<0xB1>(v);  // sum over the NG group lanes
         if constexpr (NG >= 4) v += dpp<0x4E>(v);
-        const int t = t0 + 16 * hf + 4 * q4 + r;
-        sc[hf][r] = t < r1 ? v * a.qscale : -INFINITY;
+        sc[hf][r] = v;
       }
     }
-    // ---- online softmax for this lane's head ----
-    float tm = sc[0][0];
+    if constexpr (!full) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tm = fmaxf(tm, sc[hf][r]);
+        for (int r = 0; r < 4; ++r)
+          if (t0 + 16 * hf + 4 * q4 + r >= r1) sc[hf][r] = -INFINITY;
+    }
+    // ---- online softmax for this lane's head (scores in units of qscale) ----
+    float tm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
     tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-    const float mn = fmaxf(m_run, tm);  // finite: every tile has a valid token
-    const float corr = fast_exp2(m_run - mn);
-    m_run = mn;
+    if (__builtin_amdgcn_ballot_w64(tm > m_run)) {
+      // some head's maximum grew (every tile holds a valid token, so tm is
+      // finite and the first tile always lands here)
+      const float mn = fmaxf(m_run, tm);
+      const float corr = fast_exp2((m_run - mn) * qscale);
+      m_run = mn;
+      l_run *= corr;
+      zacc *= corr;
+      // output row 4*q4 + r of the PV product is column (head, group)
+      // ((4q4 + r) / NG, (4q4 + r) % NG)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float cr = __shfl(corr, ((4 * q4 + r) / NG) * NG, 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb][r] = scale_in_place(o[nb][r], cr);
+      }
+    }
+    const float mq = m_run * qscale;
     float p[2][4], ls = 0.0f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[hf][r] = fast_exp2(sc[hf][r] - mn);
+        p[hf][r] = fast_exp2(fmaf(sc[hf][r], qscale, -mq));
         ls += p[hf][r];
       }
-    l_run = l_run * corr + ls;
+    l_run += ls;
     // ---- PV: A = p * s_V (fp16) for this lane's (head, group) row ----
     f16x8 pa;
     float zt = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int hf = i >> 2, r = i & 3;
-      const uint32_t w = vszw[hf][r];
-      const bool ok = p[hf][r] > 0.0f;  // masked tokens may carry stale scales
-      const float s = ok ? h2f_lo(w) : 0.0f, z = ok ? h2f_hi(w) : 0.0f;
+      const uint32_t w = word_of(T.vs[hf], r);
+      float s = sz_scale(w), z = sz_zero(w);
+      if constexpr (!full) {
+        // tokens past the end carry stale scale words; p is 0 there
+        const bool ok = p[hf][r] > 0.0f;
+        s = ok ? s : 0.0f;
+        z = ok ? z : 0.0f;
+      }
       pa[i] = (_Float16)(p[hf][r] * s);
       zt = fmaf(p[hf][r], z, zt);
     }
-    zacc = zacc * corr + zt;
-    // corr of the head whose rows this lane accumulates in the PV output:
-    // output row 4*q4 + r is column (head, group) = ((4q4+r)/NG, (4q4+r)%NG)
-    float corr_row[4];
+    zacc += zt;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hrow = (4 * q4 + r) / NG;
-      corr_row[r] = __shfl(corr, hrow * NG, 64);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[nb][r] *= corr_row[r];
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, nib8_to_f16(vw[nb]), o[nb], 0, 0, 0);
+    for (int nb = 0; nb < NB; ++nb)
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          pa, nib8_to_f16(word_of(T.v[nb / 4], nb % 4)), o[nb], 0, 0, 0);
+  };
+
+  // Ping-pong tiles: the next tile's loads are issued before the current tile
+  // is computed. Tiles past the range are clamped to the last tile (a cached
+  // re-read, never computed), so every load stays inside the allocation.
+  const int last_tile = ((r1 - 1) >> 5) << 5;
+  auto clamp = [&](int t) { return t < last_tile ? t : last_tile; };
+  constexpr int stride = kWaves * 32;
+  int t0 = r0 + wave * 32;
+  if (t0 < r1) {
+    I4Tile<D> ta, tb;
+    load_tile<D>(ta, kc, vc, ks, vs, t0, n16, q4, gc);
+    auto step = [&](const I4Tile<D>& T, int t) {
+      if (t + 32 <= r1) compute(T, t, BoolC<true>{});
+      else compute(T, t, BoolC<false>{});
+    };
+    for (;;) {
+      const int t1 = t0 + stride;
+      load_tile<D>(tb, kc, vc, ks, vs, clamp(t1), n16, q4, gc);
+      step(ta, t0);
+      if (t1 >= r1) break;
+      t0 = t1 + stride;
+      load_tile<D>(ta, kc, vc, ks, vs, clamp(t0), n16, q4, gc);
+      step(tb, t1);
+      if (t0 >= r1) break;
     }
   }
 
@@ -291,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   zacc += __shfl_xor(zacc, 32, 64);
   const bool wave_live = r0 + wave * 32 < r1;
   if (lane < NCOL && gc == 0 && lane / NG < G) {
-    red.m[wave][hc] = wave_live ? m_run : -INFINITY;
+    red.m[wave][hc] = wave_live ? m_run * qscale : -INFINITY;
     red.l[wave][hc] = wave_live ? l_run : 0.0f;
   }
   // zero-point term of output row 4*q4 + r, held by lane (row) --
@@ -358,44 +452,11 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     __hip_atomic_store(a.counters + hb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-static int env_split_tokens_int4() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
-    v = e ? atoi(e) : 0;
-    if (v < 0) v = 0;
-  }
-  return v;
-}
-
-template <typename K>
-static int resident_blocks_of(K kernel) {
-  int dev = 0, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess ||
-      cus <= 0 || per <= 0)
-    return 512;
-  return cus * per;
-}
-
 template <int D, int G, typename RingTag>
-static hipError_t launch_i4(Int4DecodeArgs a, int B, int64_t rows, int max_split,
+static hipError_t launch_i4(Int4DecodeArgs a, int B, int64_t rows, int st, int max_split,
                             hipStream_t s) {
-  int st = env_split_tokens_int4();
-  if (st <= 0 && a.Hr > 0) {
-    static int resident = 0;
-    if (!resident) resident = resident_blocks_of(decode_int4_kernel<D, G, RingTag>);
-    int slots = resident / B - a.Hs;
-    int per_head = slots / a.Hr;
-    if (per_head < 1) per_head = 1;
-    int64_t t = (rows + per_head - 1) / per_head;
-    st = (int)((t + 31) / 32 * 32);
-  }
-  if (st < kMinSplitTokens) st = kMinSplitTokens;
-  st = (st + 31) / 32 * 32;
   a.split_tokens = st;
-  a.n_split = (int)((rows + st - 1) / st);
+  a.n_split = a.Hr > 0 ? (int)((rows + st - 1) / st) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
   decode_int4_kernel<D, G, RingTag><<<grid, 256, 0, s>>>(a);
@@ -403,14 +464,14 @@ static hipError_t launch_i4(Int4DecodeArgs a, int B, int64_t rows, int max_split
 }
 
 template <int D, typename RingTag>
-static hipError_t launch_i4_g(int G, const Int4DecodeArgs& a, int B, int64_t rows,
+static hipError_t launch_i4_g(int G, const Int4DecodeArgs& a, int B, int64_t rows, int st,
                               int max_split, hipStream_t s) {
   switch (G) {
-    case 1: return launch_i4<D, 1, RingTag>(a, B, rows, max_split, s);
-    case 2: return launch_i4<D, 2, RingTag>(a, B, rows, max_split, s);
-    case 4: return launch_i4<D, 4, RingTag>(a, B, rows, max_split, s);
+    case 1: return launch_i4<D, 1, RingTag>(a, B, rows, st, max_split, s);
+    case 2: return launch_i4<D, 2, RingTag>(a, B, rows, st, max_split, s);
+    case 4: return launch_i4<D, 4, RingTag>(a, B, rows, st, max_split, s);
     default:
-      if constexpr (D == 64) return launch_i4<D, 8, RingTag>(a, B, rows, max_split, s);
+      if constexpr (D == 64) return launch_i4<D, 8, RingTag>(a, B, rows, st, max_split, s);
       return hipErrorInvalidValue;  // G = 8 with D = 128 exceeds 16 columns
   }
 }
@@ -427,8 +488,8 @@ hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_n
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.out = static_cast<uint16_t*>(out);
-  a.kcodes = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.k_offset);
-  a.vcodes = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.v_offset);
+  a.kcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.k_offset);
+  a.vcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.v_offset);
   a.ksz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.k_sz_offset);
   a.vsz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.v_sz_offset);
   a.kr = reinterpret_cast<uint16_t*>(L->sbuf + L->lay.ring_k_offset);
@@ -448,12 +509,14 @@ hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_n
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;
   const int B = d.batch;
+  const int st = decode_split_tokens(L, rows, 32);
+  const int ms = L->max_split;
   if (d.head_dim == 128) {
-    if (d.kv_dtype == DUO_FP16) return launch_i4_g<128, Fp16Tag>(L->G, a, B, rows, L->max_split, s);
-    return launch_i4_g<128, Bf16Tag>(L->G, a, B, rows, L->max_split, s);
+    if (d.kv_dtype == DUO_FP16) return launch_i4_g<128, Fp16Tag>(L->G, a, B, rows, st, ms, s);
+    return launch_i4_g<128, Bf16Tag>(L->G, a, B, rows, st, ms, s);
   }
-  if (d.kv_dtype == DUO_FP16) return launch_i4_g<64, Fp16Tag>(L->G, a, B, rows, L->max_split, s);
-  return launch_i4_g<64, Bf16Tag>(L->G, a, B, rows, L->max_split, s);
+  if (d.kv_dtype == DUO_FP16) return launch_i4_g<64, Fp16Tag>(L->G, a, B, rows, st, ms, s);
+  return launch_i4_g<64, Bf16Tag>(L->G, a, B, rows, st, ms, s);
 }
 
 }  // namespace duo

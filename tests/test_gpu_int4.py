@@ -24,19 +24,28 @@ def _int4_layer(Hq, Hkv, D, nr, capacity, scale, kv_dtype="fp16", S=16, R=64):
                         kv_dtype=kv_dtype, retrieval_dtype="int4", device=device())
 
 
-def _v_codes_per_token(vblocks, n):
-    """[nblk, D, 16] block layout -> [n, D] codes (token p: block p//32,
-    byte (p%32)%16, low nibble for p%32 < 16, high nibble otherwise)."""
+def _v_codes_per_token(vblocks, n, D):
+    """[nblk, 16*D] block layout -> [n, D] codes. Channel ch, token m (low
+    nibble) and m+16 (high nibble) of a block sit at byte
+    16*(4*(16*(ch//64) + ch%16) + m//4) + 4*((ch%64)//16) + m%4."""
     vb = vblocks.cpu().numpy()
-    p = np.arange(n)
+    p = np.arange(n)[:, None]
+    ch = np.arange(D)[None, :]
     blk, m, hi = p // 32, (p % 32) % 16, (p % 32) >= 16
-    byte = vb[blk, :, m]                       # [n, D]
-    return np.where(hi[:, None], byte >> 4, byte & 0xF).astype(np.uint8)
+    off = 16 * (4 * (16 * (ch // 64) + ch % 16) + m // 4) + 4 * ((ch % 64) // 16) + m % 4
+    byte = vb[blk, off]                        # [n, D]
+    return np.where(hi, byte >> 4, byte & 0xF).astype(np.uint8)
 
 
-@pytest.mark.parametrize("kv_dtype", ["fp16", "bf16"])
-def test_int4_append_codes_bit_exact(kv_dtype):
-    Hq, Hkv, D = 8, 2, 128
+def _sz_per_token(blocks, n):
+    """[nblk, D/32, 32, 2] blocked scale/zero -> [n, D/32, 2]."""
+    x = blocks.cpu().numpy().transpose(0, 2, 1, 3)  # [nblk, 32, D/32, 2]
+    return x.reshape(-1, x.shape[2], 2)[:n]
+
+
+@pytest.mark.parametrize("kv_dtype,D", [("fp16", 128), ("bf16", 128), ("fp16", 64)])
+def test_int4_append_codes_bit_exact(kv_dtype, D):
+    Hq, Hkv = 8, 2
     # single-token appends in the upper half of a 32-token block (after the
     # lower half was written) must leave the other tokens' nibbles alone
     pieces = [20, 1, 1, 30, 1, 1, 100, 5, 64, 1, 31, 1]
@@ -58,14 +67,14 @@ def test_int4_append_codes_bit_exact(kv_dtype):
     cv, sv, zv = oracle.quantize_int4_g32(v[:, 0])
     got_k = K[0, 0, :n].cpu().numpy()
     np.testing.assert_array_equal(got_k, oracle.pack_nibbles(ck))
-    np.testing.assert_array_equal(_v_codes_per_token(V[0, 0], n), cv)
-    ks = KS[0, 0, :n].cpu().numpy()
-    vs = VS[0, 0, :n].cpu().numpy()
+    np.testing.assert_array_equal(_v_codes_per_token(V[0, 0], n, D), cv)
+    ks = _sz_per_token(KS[0, 0], n)
+    vs = _sz_per_token(VS[0, 0], n)
     np.testing.assert_array_equal(ks[..., 0].view(np.uint16), sk.view(np.uint16))
     np.testing.assert_array_equal(ks[..., 1].view(np.uint16), zk.view(np.uint16))
     np.testing.assert_array_equal(vs[..., 0].view(np.uint16), sv.view(np.uint16))
     np.testing.assert_array_equal(vs[..., 1].view(np.uint16), zv.view(np.uint16))
-    say(f"  {kv_dtype}: {n} tokens of K/V codes, scales and zero-points bit-exact")
+    say(f"  {kv_dtype} D={D}: {n} tokens of K/V codes, scales and zero-points bit-exact")
 
 
 def _run_int4_decode(inp, context, steps, *, kv_dtype="fp16", label=""):
