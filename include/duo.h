@@ -87,12 +87,15 @@ typedef struct {
  * Retrieval buffer, INT4_G32 cache (cap32 = capacity rounded up to 32):
  *   K codes [B][Hr][cap32][D/2] bytes at k_offset, token-major: byte b of a
  *   row holds channel 2b in its low nibble and 2b+1 in its high nibble.
- *   V codes [B][Hr][cap32/32][D][16] bytes at v_offset, in 32-token blocks:
- *   byte m of channel row d of a block holds token m of the block in its low
- *   nibble and token m+16 in its high nibble.
- *   K scale/zero [B][Hr][cap32][D/32][2] fp16 (scale, zero) at k_sz_offset,
- *   V scale/zero likewise at v_sz_offset. A value decodes as
- *   fma(code, scale, zero) in fp32.
+ *   V codes [B][Hr][cap32/32][16*D] bytes at v_offset, in 32-token blocks:
+ *   for channel c and m in [0,16), the byte at offset
+ *   16*(4*(16*(c/64) + c%16) + m/4) + 4*((c%64)/16) + m%4 of a block holds
+ *   token m of the block in its low nibble and token m+16 in its high nibble.
+ *   K scale/zero [B][Hr][cap32/32][D/32][32] words at k_sz_offset (block,
+ *   32-channel group, token within the block), each word two fp16 values:
+ *   scale in the low half, zero-point in the high half; V scale/zero likewise
+ *   at v_sz_offset. A value decodes as fma(code, scale, zero) in fp32.
+ *   One head's code array must stay below 2^31 bytes (cap32 * D/2 < 2^31).
  * Streaming buffer: ring K [B][Hs][S+R][D] kv_dtype at ring_k_offset, ring V
  *   at ring_v_offset, Hs = Hkv - Hr. Token position p lives in slot p if
  *   p < S, else in slot S + ((p - S) mod R).

@@ -84,6 +84,10 @@ static duo_status check_desc(const duo_layer_desc* d) {
   // the 4-bit decode kernel maps (query head, channel group) pairs of a KV
   // head onto the 16 columns of one MFMA tile
   if (d->retrieval_dtype == DUO_INT4_G32 && G * (d->head_dim / 32) > 16) return DUO_ERR_UNSUPPORTED;
+  // ... and addresses one head's code array with 32-bit offsets
+  if (d->retrieval_dtype == DUO_INT4_G32 &&
+      cap32_of(d->retrieval_capacity) * (d->head_dim / 2) >= ((int64_t)1 << 31))
+    return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 

@@ -66,11 +66,22 @@ def test_layout_sizes():
     (dict(softmax_scale=float("inf")), 1),
     (dict(softmax_scale=0.0), 1),
     (dict(softmax_scale=-0.1), 1),
+    # 4-bit cache: one head's code array must stay below 2^31 bytes
+    (dict(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25)), 2),
 ])
 def test_bad_descriptor_rejected(kw, status):
     L = _lib()
     out = L.Layout()
     assert L.lib.duo_layer_layout(ctypes.byref(_desc(**kw)), ctypes.byref(out)) == status
+
+
+def test_int4_capacity_limit():
+    L = _lib()
+    out = L.Layout()
+    ok = _desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25) - 32)
+    assert L.lib.duo_layer_layout(ctypes.byref(ok), ctypes.byref(out)) == 0
+    big = _desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25) - 31)
+    assert L.lib.duo_layer_layout(ctypes.byref(big), ctypes.byref(out)) == 2
 
 
 def test_init_validates_before_any_hip_call():
