@@ -116,10 +116,13 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
   constexpr int KPAD = D + 8;         // K tile row stride in LDS (elements)
   constexpr int KLD = D / 32;         // 16-byte K loads per thread
   constexpr bool kMixed = MODE == MODE_MIXED;
-  __shared__ __align__(16) uint16_t Ks[kBN * KPAD];
-  __shared__ __align__(16) uint16_t Vt[D * kBN];
+  // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
+  // written to the other, so one barrier per tile suffices
+  __shared__ __align__(16) uint16_t Ks[2][kBN * KPAD];
+  __shared__ __align__(16) uint16_t Vt[2][D * kBN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h2 = lane >> 5, q32 = lane & 31;
   const int b = blockIdx.z;
   const int groups = a.G / HB;
@@ -176,9 +179,11 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
         vreg[r] = ld16(KeySrc<D>::template row<MODE>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    uint16_t* ks = Ks[stage];
+    uint16_t* vt = Vt[stage];
 #pragma unroll
-    for (int c = 0; c < KLD; ++c) st16(Ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+    for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
     if (v_active) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
         uint32_t lo = __builtin_amdgcn_perm(word_of(vreg[1], i >> 1), word_of(vreg[0], i >> 1), sel);
         uint32_t hi = __builtin_amdgcn_perm(word_of(vreg[3], i >> 1), word_of(vreg[2], i >> 1), sel);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + d * kBN + 4 * vt_slot(vg, d));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vt + d * kBN + 4 * vt_slot(vg, d));
         dst[0] = lo;
         dst[1] = hi;
       }
@@ -243,44 +248,63 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)p[s >> 1][8 * (s & 1) + i];
   };
-  auto pv = [&](const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
+  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
+    // all V^T fragments of two 16-key slices are requested before their
+    // products (the empty asm keeps the compiler from sinking each read next
+    // to its use, which would expose the LDS latency between products)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 av[DB];
+    for (int s2 = 0; s2 < 4; s2 += 2) {
+      bf16x8 av[2][DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
-        const int d = 32 * db + q32;
-        av[db] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + d * kBN + 4 * vt_slot(4 * s + h2, d)));
-      }
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], pb[s], O[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
+          const int d = 32 * db + q32;
+          av[h][db] = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(vt + d * kBN + 4 * vt_slot(4 * (s2 + h) + h2, d)));
+        }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[h][db], pb[s2 + h], O[db], 0, 0, 0);
     }
   };
 
   // ---- main loop ----------------------------------------------------------------
   load_tile(tile_pos(0));
-  store_tile();
+  store_tile(0);
   __syncthreads();
   for (int k = 0; k < ntiles; ++k) {
     const int p0 = tile_pos(k);
+    const int stage = k & 1;
     const bool more = k + 1 < ntiles;
     if (more) load_tile(tile_pos(k + 1));
 
-    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
-    f32x16 st[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-      const uint16_t* krow = Ks + (32 * kb + q32) * KPAD + 8 * h2;
-      bf16x8 ak[KS];
+    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks). All K
+    // fragments of a block are requested before its first product (as for V
+    // above), and the two blocks' independent accumulation chains are
+    // interleaved.
+    f32x16 st[2] = {f32x16{}, f32x16{}};
+    {
+      const uint16_t* krow0 = Ks[stage] + q32 * KPAD + 8 * h2;
+      const uint16_t* krow1 = krow0 + 32 * KPAD;
+      bf16x8 ak0[KS], ak1[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
+        ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qf[ks], st[kb], 0, 0, 0);
+        ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
+      }
     }
     // raw scores with this mode's mask; tiles wholly below the wave's first
     // query need no causal mask, tiles wholly above its last query are skipped
@@ -314,20 +338,18 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
       }
       bf16x8 pb[4];
       softmax_update(sf, m_f, l_f, o_f, pb);
-      pv(pb, o_f);
+      pv(Vt[stage], pb, o_f);
       if constexpr (kMixed) {
         if (lam_tile) {
           bf16x8 pl[4];
           softmax_update(sl, m_l, l_l, o_l, pl);
-          pv(pl, o_l);
+          pv(Vt[stage], pl, o_l);
         }
       }
     }
-    __syncthreads();  // every wave is done with this tile's LDS
-    if (more) {
-      store_tile();
-      __syncthreads();
-    }
+    // the other stage was last read before the previous barrier
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
   }
 
   // ---- epilogue -----------------------------------------------------------------
