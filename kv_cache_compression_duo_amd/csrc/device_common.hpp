@@ -37,8 +37,12 @@ __device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
 }
 
 // ---- element types ---------------------------------------------------------
-struct Bf16Tag {};
-struct Fp16Tag {};
+struct Bf16Tag {
+  static constexpr bool is_bf16 = true;
+};
+struct Fp16Tag {
+  static constexpr bool is_bf16 = false;
+};
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

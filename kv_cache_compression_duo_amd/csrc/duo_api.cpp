@@ -120,7 +120,9 @@ duo_status duo_layer_layout(const duo_layer_desc* d, duo_layout* out) {
     L.k_offset = 0;
     L.v_offset = arr;
     L.k_sz_offset = L.v_sz_offset = 0;
-    L.retrieval_bytes = 2 * arr;
+    // the decode kernel reads whole row tiles from any valid start row, so
+    // the buffer extends kDecodePadRows rows past the last V row
+    L.retrieval_bytes = Hr ? 2 * arr + align_up((size_t)kDecodePadRows * D * 2, 256) : 0;
   }
   size_t ring = align_up(B * Hs * W * D * 2, 256);
   L.ring_k_offset = 0;

@@ -22,6 +22,9 @@ namespace duo {
 // Workspace layout: [counters: B*Hr u32, padded to 256 B][m,l: B*Hr*G*max_split*2 f32]
 //                   [acc: B*Hr*G*max_split*D f32]
 constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
+// Rows of readable (never used) memory after a bf16/fp16 retrieval buffer: a
+// decode tile of 32 rows starting at any valid row stays inside the buffer.
+constexpr int kDecodePadRows = 32;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // 4-bit caches are allocated in whole 32-token blocks.

@@ -47,11 +47,14 @@ struct DecodeArgs {
   float qscale;           // softmax scale * log2(e)
 };
 
+constexpr int kDecodeWaves = 4;  // waves per block
+
 template <int D, int G, typename Tag>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;
-  __shared__ BlockRed<D, G> red;
-  __shared__ MergeLds mlds;
+  constexpr int NW = kDecodeWaves;
+  __shared__ BlockRed<D, G, NW> red;
+  __shared__ MergeLds<64 * NW> mlds;
   __shared__ int is_last;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -85,15 +88,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const uint16_t* kc = a.kc + hb * a.cap * D;
     const uint16_t* vc = a.vc + hb * a.cap * D;
     const int n = a.n;
-    auto kp = [=](int row) { return row == n ? knew : kc + (int64_t)row * D; };
-    auto vp = [=](int row) { return row == n ? vnew : vc + (int64_t)row * D; };
-    attend_rows<D, G, Tag>(st, qf, r0, r1, kp, vp);
+    // cache rows [r0, min(r1, n)); the split holding position n adds the
+    // new token from its input
+    const bool has_new = r1 == n + 1;
+    QFrag<G> qfrag;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const u32x4 raw = ld16(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + lc * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qfrag.w[g][i] = word_of(raw, i);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qfrag.f[g][c] = qf[g][c];
+    }
+    attend_cache<D, G, Tag, NW>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, r0,
+                            has_new ? n : r1, knew, vnew, has_new);
     // the new token's cache row (read by no block of this launch)
     if (split == 0 && threadIdx.x < LPR) {
       st16(a.kc + (hb * a.cap + n) * D + threadIdx.x * 8, ld16(knew + threadIdx.x * 8));
       st16(a.vc + (hb * a.cap + n) * D + threadIdx.x * 8, ld16(vnew + threadIdx.x * 8));
     }
-    block_merge<D, G>(red, st);
+    block_merge<D, G, NW>(red, st);
     // Publish this split's partial state. The partials are written and read
     // with agent-scope (cache-coherent) accesses and the writes are drained
     // before the arrival count is bumped, so no cache-wide writeback or
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (!is_last) return;
     // last block of this head: merge all splits
-    merge_splits<D, G>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
+    merge_splits<D, G, 64 * NW>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
                        a.out + ((int64_t)b * a.Hq + kvh * G) * D);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + hb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -136,12 +150,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const uint16_t* vr = a.vr + hb * W * D;
     auto kp = [=](int row) { return row == slot_new ? knew : kr + (int64_t)row * D; };
     auto vp = [=](int row) { return row == slot_new ? vnew : vr + (int64_t)row * D; };
-    attend_rows<D, G, Tag>(st, qf, 0, nslots, kp, vp);
+    attend_rows<D, G, Tag, NW>(st, qf, 0, nslots, kp, vp);
     if (threadIdx.x < LPR) {
       st16(a.kr + (hb * W + slot_new) * D + threadIdx.x * 8, ld16(knew + threadIdx.x * 8));
       st16(a.vr + (hb * W + slot_new) * D + threadIdx.x * 8, ld16(vnew + threadIdx.x * 8));
     }
-    block_merge<D, G>(red, st);
+    block_merge<D, G, NW>(red, st);
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
       int g = i / D, dd = i % D;
       a.out[((int64_t)b * a.Hq + kvh * G + g) * D + dd] =
@@ -157,7 +171,7 @@ static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int split_tokens, 
   a.n_split = a.Hr > 0 ? (int)((rows + split_tokens - 1) / split_tokens) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
-  decode_kernel<D, G, Tag><<<grid, 256, 0, s>>>(a);
+  decode_kernel<D, G, Tag><<<grid, 64 * kDecodeWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -200,7 +214,7 @@ hipError_t launch_decode(const duo_layer* L, const void* q, const void* k_new,
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;
   const int B = d.batch;
-  const int st = decode_split_tokens(L, rows, kTile);
+  const int st = decode_split_tokens(L, rows, 1);
   const int ms = L->max_split;
   if (d.head_dim == 128) {
     if (d.kv_dtype == DUO_FP16) return launch_g<128, Fp16Tag>(L->G, a, B, rows, st, ms, s);

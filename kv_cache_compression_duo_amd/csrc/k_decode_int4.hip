@@ -162,14 +162,19 @@ __device__ __forceinline__ void load_tile(I4Tile<D>& T, const uint8_t* __restric
   }
 }
 
+// Waves per block: two waves per SIMD let one wave's dequantisation overlap
+// another's loads (the tile loop is VALU-heavy).
+constexpr int kI4Waves = 8;
+
 template <int D, int G, typename RingTag>
-__global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
+__global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeArgs a) {
+  constexpr int NW = kI4Waves;
   constexpr int NG = D / 32;     // channel groups
   constexpr int NCOL = G * NG;   // used MFMA columns (head, group)
   constexpr int NB = D / 16;     // 16-channel n-blocks of the PV product
   static_assert(NCOL <= 16, "G * D / 32 must fit 16 MFMA columns");
-  __shared__ BlockRed<D, G> red;
-  __shared__ MergeLds mlds;
+  __shared__ BlockRed<D, G, NW> red;
+  __shared__ MergeLds<64 * NW> mlds;
   __shared__ int is_last;
 
   const int b = blockIdx.y;
@@ -203,12 +208,12 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
     auto kp = [=](int row) { return row == slot_new ? knew : kr + (int64_t)row * D; };
     auto vp = [=](int row) { return row == slot_new ? vnew : vr + (int64_t)row * D; };
     WaveState<G> st;
-    attend_rows<D, G, RingTag>(st, qf, 0, nslots, kp, vp);
+    attend_rows<D, G, RingTag, NW>(st, qf, 0, nslots, kp, vp);
     if (threadIdx.x < LPR) {
       st16(a.kr + (hb * Wr + slot_new) * D + threadIdx.x * 8, ld16(knew + threadIdx.x * 8));
       st16(a.vr + (hb * Wr + slot_new) * D + threadIdx.x * 8, ld16(vnew + threadIdx.x * 8));
     }
-    block_merge<D, G>(red, st);
+    block_merge<D, G, NW>(red, st);
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
       int g = i / D, dd = i % D;
       a.out[((int64_t)b * a.Hq + kvh * G + g) * D + dd] =
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   // re-read, never computed), so every load stays inside the allocation.
   const int last_tile = ((r1 - 1) >> 5) << 5;
   auto clamp = [&](int t) { return t < last_tile ? t : last_tile; };
-  constexpr int stride = kWaves * 32;
+  constexpr int stride = NW * 32;
   int t0 = r0 + wave * 32;
   if (t0 < r1) {
     I4Tile<D> ta, tb;
@@ -407,9 +412,9 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float M = red.m[0][g];
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red.m[w][g]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red.m[w][g]);
     float Lsum = 0.0f;
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < NW; ++w)
       Lsum += red.m[w][g] == -INFINITY ? 0.0f : red.l[w][g] * fast_exp2(red.m[w][g] - M);
     red.M[g] = M;
     red.L[g] = Lsum;
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int g = i / D, dd = i % D;
     float s = 0.0f;
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < NW; ++w)
       if (red.m[w][g] != -INFINITY) s += red.acc[w][g][dd] * fast_exp2(red.m[w][g] - red.M[g]);
     red.acc[0][g][dd] = s;  // each (g, dd) is read and written by one thread only
   }
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(256) void decode_int4_kernel(Int4DecodeArgs a) {
   }
   __syncthreads();
   if (!is_last) return;
-  merge_splits<D, G>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
+  merge_splits<D, G, 64 * NW>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
                      a.out + ((int64_t)b * a.Hq + kvh * G) * D);
   if (threadIdx.x == 0)
     __hip_atomic_store(a.counters + hb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -459,7 +464,7 @@ static hipError_t launch_i4(Int4DecodeArgs a, int B, int64_t rows, int st, int m
   a.n_split = a.Hr > 0 ? (int)((rows + st - 1) / st) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
-  decode_int4_kernel<D, G, RingTag><<<grid, 256, 0, s>>>(a);
+  decode_int4_kernel<D, G, RingTag><<<grid, 64 * kI4Waves, 0, s>>>(a);
   return hipGetLastError();
 }
 

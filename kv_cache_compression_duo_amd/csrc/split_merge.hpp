@@ -11,60 +11,70 @@
 
 namespace duo {
 
-constexpr int kMergeThreads = 256;
-
+// Scratch of a merge by a block of NT threads.
+template <int NT>
 struct MergeLds {
-  float w[2 * kMergeThreads];
-  float part[kMergeThreads];
+  float w[2 * NT];
+  float part[NT];
 };
 
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ float2 ld_agent2(const float* p) {  // 8-byte aligned
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 // ml: [G][max_split][2], acc: [G][max_split][D]; out row g at out + g*D (bf16).
 // Thread (part, d) folds the splits part, part + P, ... into a running
-// (m, l, o). Loads are issued UN splits at a time with clamped (always valid)
-// addresses, so a batch costs one memory round trip; entries past the last
-// split get weight 0. The P parts of each channel are then folded in LDS.
-template <int D, int G>
-__device__ void merge_splits(MergeLds& s, const float* __restrict__ ml,
+// (m, l, o). D is a multiple of 64, so `part` is uniform in a wave and the
+// split indices and addresses are scalar. Loads are issued UN splits at a
+// time with clamped (always valid) indices, so a batch costs one memory round
+// trip; entries past the last split get weight 0. The P parts of each channel
+// are then folded in LDS.
+template <int D, int G, int NT>
+__device__ void merge_splits(MergeLds<NT>& s, const float* __restrict__ ml,
                              const float* __restrict__ acc, int max_split, int n_split,
                              uint16_t* __restrict__ out) {
-  constexpr int P = kMergeThreads / D;  // threads per output channel
+  constexpr int P = NT / D;  // threads per output channel
   constexpr int UN = 16;
+  static_assert(D % 64 == 0, "a wave must not straddle two parts");
   const int t = threadIdx.x;
-  const int d = t % D, part = t / D;
+  const int d = t % D;
+  const int part = __builtin_amdgcn_readfirstlane(t / D);
   for (int g = 0; g < G; ++g) {
     const float* mlg = ml + (int64_t)g * max_split * 2;
     const float* ag = acc + (int64_t)g * max_split * D + d;
     float m = -INFINITY, l = 0.0f, o = 0.0f;
     for (int sp0 = part; sp0 < n_split; sp0 += UN * P) {
-      float mm[UN], ll[UN], aa[UN];
+      float2 mlv[UN];
+      float aa[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int sp = sp0 + u * P < n_split ? sp0 + u * P : n_split - 1;
-        mm[u] = ld_agent(mlg + sp * 2);
-        ll[u] = ld_agent(mlg + sp * 2 + 1);
+        mlv[u] = ld_agent2(mlg + sp * 2);
         aa[u] = ld_agent(ag + (int64_t)sp * D);
       }
       float mx = m;
 #pragma unroll
-      for (int u = 0; u < UN; ++u) mx = fmaxf(mx, mm[u]);
+      for (int u = 0; u < UN; ++u) mx = fmaxf(mx, mlv[u].x);
       const float c = fast_exp2(m - mx);  // m = -inf on the first batch -> 0
       l *= c;
       o *= c;
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const float w = sp0 + u * P < n_split ? fast_exp2(mm[u] - mx) : 0.0f;
-        l = fmaf(ll[u], w, l);
+        const float w = sp0 + u * P < n_split ? fast_exp2(mlv[u].x - mx) : 0.0f;
+        l = fmaf(mlv[u].y, w, l);
         o = fmaf(aa[u], w, o);
       }
       m = mx;
     }
     s.part[t] = m;
     s.w[t] = l;
-    s.w[kMergeThreads + t] = o;
+    s.w[NT + t] = o;
     __syncthreads();
     if (t < D) {
       float M = s.part[t];
@@ -76,7 +86,7 @@ __device__ void merge_splits(MergeLds& s, const float* __restrict__ ml,
         const float mp = s.part[p * D + t];
         const float w = mp == -INFINITY ? 0.0f : fast_exp2(mp - M);
         L = fmaf(s.w[p * D + t], w, L);
-        O = fmaf(s.w[kMergeThreads + p * D + t], w, O);
+        O = fmaf(s.w[NT + p * D + t], w, O);
       }
       out[(int64_t)g * D + t] = (uint16_t)f2bf(O / L);
     }

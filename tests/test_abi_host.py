@@ -38,7 +38,8 @@ def _desc(**kw):
 def test_layout_sizes():
     L = _lib()
     lay = L.layout(_desc())
-    assert lay.retrieval_bytes == 2 * 4 * 1000 * 128 * 2
+    # K and V arrays, then 32 readable rows (decode tiles start at any row)
+    assert lay.retrieval_bytes == 2 * 4 * 1000 * 128 * 2 + 32 * 128 * 2
     assert lay.v_offset == 4 * 1000 * 128 * 2
     assert lay.streaming_bytes == 2 * 4 * 80 * 128 * 2
     lay4 = L.layout(_desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=1024))
@@ -52,6 +53,8 @@ def test_layout_sizes():
     for x in (lay, lay4):
         for f in ("v_offset", "k_sz_offset", "v_sz_offset", "ring_v_offset"):
             assert getattr(x, f) % 256 == 0
+    # no retrieval heads: no retrieval buffer
+    assert L.layout(_desc(n_retrieval_kv_heads=0)).retrieval_bytes == 0
 
 
 @pytest.mark.parametrize("kw,status", [
