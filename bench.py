@@ -87,6 +87,114 @@ def time_region(torch, fn, reps=1):
     return a.elapsed_time(b) / reps
 
 
+# ---- measured HBM traffic (rocprofv3 counters) -------------------------------------
+# The decode kernel's HBM bytes per launch come from two rocprofv3 --pmc runs of
+# `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+# each scaled by what the same counter reads for a device copy of known size in
+# the same run. `bench.py --traffic-summary FETCH_DIR WRITE_DIR` turns the two
+# runs into profiles/decode_kernel_llama2_7b_32k_traffic.json (+ .md). The
+# figure is reported only while the decode kernel's sources hash to the value
+# recorded with it.
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_32k_traffic.json")
+DECODE_SOURCES = ["k_decode.hip", "decode_common.hpp", "split_merge.hpp", "device_common.hpp",
+                  "duo_api.cpp", "duo_internal.hpp"]
+COPY_BYTES = 256 << 20
+DECODE_KERNEL = "decode_kernel<128, 1, duo::Bf16Tag>"
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_compression_duo_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != decode_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return t.get("bytes_per_launch")
+
+
+def traffic_probe(dev):
+    """Launches profiled by the two counter runs: decode steps of one layer of
+    the headline workload, then a plain device copy of COPY_BYTES."""
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+
+    w = WORKLOADS["llama2_7b_decode_32k"]
+    Hq, Hkv, D, Hr = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_retrieval_kv
+    steps = 6
+    lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
+                       capacity=w.context + steps, softmax_scale=w.softmax_scale, device=dev)
+    for a in range(0, w.context, 8192):
+        lay.append_kv(device_normal((1, 8192, Hkv, D), 7000 + a // 8192, dev, torch.bfloat16),
+                      device_normal((1, 8192, Hkv, D), 9000 + a // 8192, dev, torch.bfloat16))
+    q = (device_normal((steps, 1, 1, Hq, D), 11, dev, torch.float32) / math.sqrt(D)).to(torch.bfloat16)
+    kn = device_normal((steps, 1, 1, Hkv, D), 12, dev, torch.bfloat16)
+    vn = device_normal((steps, 1, 1, Hkv, D), 13, dev, torch.bfloat16)
+    out = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    for s in range(steps):
+        lay.decode(q[s], kn[s], vn[s], out)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# traffic probe: {steps} decode launches, 3 copies of {COPY_BYTES} bytes",
+          file=sys.stderr, flush=True)
+
+
+def _pmc_means(run_dir, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 csv run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def traffic_summary(fetch_dir, write_dir):
+    fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
+    write = _pmc_means(write_dir, "WRITE_SIZE")
+    def pick(d, key):
+        names = [k for k in d if key in k]
+        if len(names) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
+        return names[0], d[names[0]]
+    dec_name, f_dec = pick(fetch, DECODE_KERNEL)
+    _, w_dec = pick(write, DECODE_KERNEL)
+    copy_name, f_copy = pick(fetch, "__amd_rocclr_copyBuffer")
+    _, w_copy = pick(write, "__amd_rocclr_copyBuffer")
+    kib = COPY_BYTES / 1024.0
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    fetch_b = f_dec * f_scale * 1024.0
+    write_b = w_dec * w_scale * 1024.0
+    t = {"kernel": dec_name, "workload": "llama2_7b_decode_32k",
+         "fetch_kib_per_launch": f_dec, "write_kib_per_launch": w_dec,
+         "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
+         "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+         "fetch_scale": f_scale, "write_scale": w_scale,
+         "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+         "bytes_per_launch": fetch_b + write_b, "source_hash": decode_source_hash()}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(t, fh, indent=1)
+    print(json.dumps(t, indent=1))
+
+
 # ---- workloads -------------------------------------------------------------------
 def bench_decode_llama2(args, dev):
     import torch
@@ -139,7 +247,7 @@ def bench_decode_llama2(args, dev):
         "value": gbs, "ms_per_step": ms_step, "tok_per_s": 1000.0 / ms_step,
         "bytes_per_step": nbytes / args.steps, "layers_cycled": L,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "duo::decode_kernel<128, 1, duo::Bf16Tag>",
                      "avg_launch_us": ms_step * 1e3},
     }
@@ -315,13 +423,23 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of: decode,mha8,prefill,mixed,int4")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only the launches the counter runs measure")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 csv runs into the traffic record")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build",
               file=sys.stderr)
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")
+    if args.traffic_probe:
+        traffic_probe(dev)
+        return
     only = set(x for x in args.only.split(",") if x)
     want = lambda name: not only or name in only
     line = {
