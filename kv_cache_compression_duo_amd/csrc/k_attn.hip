@@ -17,9 +17,10 @@
 // the kernel below is a gfx950 design of the same exact computation.
 //
 // gfx950 design:
-//   * a block is 4 waves; a wave owns 32 query rows (32 tokens of one query
-//     head). The HB heads of a block share one KV head (GQA grouping), so one
-//     K/V tile in LDS serves up to 4 query heads;
+//   * a block is 8 waves (prefill) or 4 (mixed forward); a wave owns 32
+//     query rows (32 tokens of one query head). The HB heads of a block share
+//     one KV head (GQA grouping), so one K/V tile in LDS serves up to 8 waves
+//     of query rows; in an 8-wave block half the waves stage K and half V;
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16. In this
 //     orientation a lane holds one query's scores, so the softmax needs one
 //     cross-lane exchange per tile, and the score accumulator is directly the
@@ -107,12 +108,19 @@ struct KeySrc {
   }
 };
 
+// Waves per block: 8 for the prefill modes (each staged K/V tile then serves
+// 256 query rows; waves 0-3 stage V, waves 4-7 stage K), 4 for the mixed
+// forward, whose two sets of accumulators leave room for one wave per SIMD.
+template <int MODE>
+constexpr int attn_waves() { return MODE == MODE_MIXED ? 4 : 8; }
+
 template <int D, int HB, int MODE>
-__global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnArgs a) {
+  constexpr int NW = attn_waves<MODE>();
   constexpr int KS = D / 16;          // k-steps of the QK product
   constexpr int DB = D / 32;          // 32-row d-blocks of the PV product
   constexpr int TOKW = 32;            // tokens per wave
-  constexpr int BMT = TOKW * 4 / HB;  // tokens per block
+  constexpr int BMT = TOKW * NW / HB;  // tokens per block
   constexpr int KPAD = D + 8;         // K tile row stride in LDS (elements)
   constexpr int KLD = D / 32;         // 16-byte K loads per thread
   constexpr bool kMixed = MODE == MODE_MIXED;
@@ -165,14 +173,22 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
   }
 
   // ---- global -> register staging of one K/V tile ------------------------------
-  const int kr_row = tid >> 2, kr_d0 = (tid & 3) * (D / 4);
-  const int vg = tid & 15, vdc = tid >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
-  const bool v_active = vdc < D / 8;
+  // 256 threads stage K and 256 stage V (one set of 256 does both when the
+  // block has 4 waves); the roles are wave-uniform.
+  constexpr bool kSplitStage = NW == 8;
+  const int st_t = tid & 255;
+  const bool stage_k = !kSplitStage || wave >= 4;
+  const bool stage_v = !kSplitStage || wave < 4;
+  const int kr_row = st_t >> 2, kr_d0 = (st_t & 3) * (D / 4);
+  const int vg = st_t & 15, vdc = st_t >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
+  const bool v_active = stage_v && vdc < D / 8;
   u32x4 kreg[KLD], vreg[4];
   auto load_tile = [&](int p0) {
-    const uint16_t* kp = KeySrc<D>::template row<MODE>(a, b, kv, p0 + kr_row, false) + kr_d0;
+    if (stage_k) {
+      const uint16_t* kp = KeySrc<D>::template row<MODE>(a, b, kv, p0 + kr_row, false) + kr_d0;
 #pragma unroll
-    for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
+      for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
+    }
     if (v_active) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -182,8 +198,10 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
   auto store_tile = [&](int stage) {
     uint16_t* ks = Ks[stage];
     uint16_t* vt = Vt[stage];
+    if (stage_k) {
 #pragma unroll
-    for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+      for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+    }
     if (v_active) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -383,11 +401,12 @@ __global__ __launch_bounds__(256, MODE == MODE_MIXED ? 1 : 2) void attn_kernel(A
 // ---- launchers -------------------------------------------------------------------
 template <int D, int HB, int MODE>
 static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
-  constexpr int BMT = 32 * 4 / HB;
+  constexpr int NW = attn_waves<MODE>();
+  constexpr int BMT = 32 * NW / HB;
   AttnArgs x = a;
   x.n_qtiles = (a.T + BMT - 1) / BMT;
   dim3 grid((unsigned)x.n_qtiles, (unsigned)(n_kv * (a.G / HB)), (unsigned)B);
-  attn_kernel<D, HB, MODE><<<grid, 256, 0, s>>>(x);
+  attn_kernel<D, HB, MODE><<<grid, 64 * NW, 0, s>>>(x);
   return hipGetLastError();
 }
 
