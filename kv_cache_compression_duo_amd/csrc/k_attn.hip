@@ -17,10 +17,15 @@
 // the kernel below is a gfx950 design of the same exact computation.
 //
 // gfx950 design:
-//   * a block is 8 waves (prefill) or 4 (mixed forward); a wave owns 32
-//     query rows (32 tokens of one query head). The HB heads of a block share
-//     one KV head (GQA grouping), so one K/V tile in LDS serves up to 8 waves
-//     of query rows; in an 8-wave block half the waves stage K and half V;
+//   * a block is 8 waves; a wave owns 32 query rows (32 tokens of one query
+//     head). The HB heads of a block share one KV head (GQA grouping), so one
+//     K/V tile in LDS serves 8 waves of query rows; half the waves stage K and
+//     half V;
+//   * the mixed forward runs in two phases over one tile pipeline and one
+//     softmax state: the Lambda tiles (sinks and the window band, a few per
+//     query tile) first, folded into (1 - alpha) * O / l kept as bf16 pairs,
+//     then all causal tiles as in retrieval mode (the band's QK products are
+//     computed twice; two sets of accumulators would halve the occupancy);
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16. In this
 //     orientation a lane holds one query's scores, so the softmax needs one
 //     cross-lane exchange per tile, and the score accumulator is directly the
@@ -108,11 +113,10 @@ struct KeySrc {
   }
 };
 
-// Waves per block: 8 for the prefill modes (each staged K/V tile then serves
-// 256 query rows; waves 0-3 stage V, waves 4-7 stage K), 4 for the mixed
-// forward, whose two sets of accumulators leave room for one wave per SIMD.
+// Waves per block: 8 (each staged K/V tile serves 256 query rows; waves 0-3
+// stage V, waves 4-7 stage K).
 template <int MODE>
-constexpr int attn_waves() { return MODE == MODE_MIXED ? 4 : 8; }
+constexpr int attn_waves() { return 8; }
 
 template <int D, int HB, int MODE>
 __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnArgs a) {
@@ -149,20 +153,23 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const int i_wlast = a.n + (w_tok0 + TOKW - 1 < a.T ? w_tok0 + TOKW - 1 : a.T - 1);
 
   // ---- key tiles visited by this block --------------------------------------
-  int n1, w0, ntiles;
-  if constexpr (MODE == MODE_STREAMING) {
+  // Lambda tiles (the sink tiles, then the window tiles of the block's
+  // queries) come first: they are the whole sequence in streaming mode and
+  // phase 1 of the mixed forward; the causal tiles follow (retrieval mode,
+  // phase 2 of the mixed forward).
+  int n1 = 0, w0 = 0, nlam = 0, ntiles;
+  if constexpr (MODE != MODE_RETRIEVAL) {
     const int lo = i_min - a.R + 1 > 0 ? i_min - a.R + 1 : 0;
     const int sink_hi = a.S < i_max + 1 ? a.S : i_max + 1;
     n1 = (sink_hi + kBN - 1) / kBN;  // sink tiles cover [0, 64*n1)
     w0 = lo > kBN * n1 ? lo : kBN * n1;
     const int n2 = i_max >= w0 ? (i_max - w0) / kBN + 1 : 0;
-    ntiles = n1 + n2;
-  } else {
-    n1 = 0;
-    w0 = 0;
-    ntiles = i_max / kBN + 1;
+    nlam = n1 + n2;
   }
-  auto tile_pos = [&](int k) { return k < n1 ? kBN * k : w0 + kBN * (k - n1); };
+  ntiles = MODE == MODE_STREAMING ? nlam : nlam + i_max / kBN + 1;
+  auto tile_pos = [&](int k) {
+    return k < nlam ? (k < n1 ? kBN * k : w0 + kBN * (k - n1)) : kBN * (k - nlam);
+  };
 
   // ---- query fragments (B operand of S^T = K Q^T) ----------------------------
   bf16x8 qf[KS];
@@ -217,16 +224,15 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   };
 
   // ---- state --------------------------------------------------------------------
+  // One softmax state (m, l, O). The mixed forward runs its Lambda phase in
+  // it, folds (1 - alpha) * O / l into lam_pk (bf16 pairs) and restarts it for
+  // the causal phase, so it never holds two sets of accumulators.
   f32x16 o_f[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
   float m_f = -INFINITY, l_f = 0.0f;
-  f32x16 o_l[kMixed ? DB : 1];
-  float m_l = -INFINITY, l_l = 0.0f;
-  if constexpr (kMixed) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o_l[db] = f32x16{};
-  }
+  uint32_t lam_pk[kMixed ? DB : 1][8];
+  const float alpha = kMixed ? a.alpha[kv] : 1.0f;
 
   // One online-softmax update of (m, l, O) from masked raw scores (m in raw
   // score units; the scale, folded with log2(e), enters the exp2 argument as
@@ -300,6 +306,21 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     const int stage = k & 1;
     const bool more = k + 1 < ntiles;
     if (more) load_tile(tile_pos(k + 1));
+    if (kMixed && k == nlam) {
+      // end of the Lambda phase: keep (1 - alpha) * O / l, restart the state
+      const float ll = l_f + __shfl_xor(l_f, 32, 64);
+      const float wl = (1.0f - alpha) / ll;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          lam_pk[db][i] = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
+        o_f[db] = f32x16{};
+      }
+      m_f = -INFINITY;
+      l_f = 0.0f;
+    }
+    const bool lam_phase = MODE == MODE_STREAMING || (kMixed && k < nlam);
 
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks). All K
     // fragments of a block are requested before its first product (as for V
@@ -309,44 +330,53 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     {
       const uint16_t* krow0 = Ks[stage] + q32 * KPAD + 8 * h2;
       const uint16_t* krow1 = krow0 + 32 * KPAD;
-      bf16x8 ak0[KS], ak1[KS];
+      if constexpr (!kMixed) {
+        bf16x8 ak0[KS], ak1[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
-      asm volatile("" ::: "memory");
+        for (int ks = 0; ks < KS; ++ks)
+          ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
+        asm volatile("" ::: "memory");
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
-      asm volatile("" ::: "memory");
+        for (int ks = 0; ks < KS; ++ks)
+          ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
+        asm volatile("" ::: "memory");
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
+          st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
+        }
+      } else {
+        // the mixed forward also holds its Lambda result: one 32-key block's
+        // fragments at a time
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint16_t* krow = kb ? krow1 : krow0;
+          bf16x8 ak[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qf[ks], st[kb], 0, 0, 0);
+        }
       }
     }
     // raw scores with this mode's mask; tiles wholly below the wave's first
     // query need no causal mask, tiles wholly above its last query are skipped
     const bool live = p0 <= i_wlast;
     const bool diag = p0 + kBN - 1 > i_wfirst;
-    const bool lam_tile = kMixed && (p0 < a.S || p0 + kBN - 1 >= i_min - a.R + 1);
     if (live) {
       float sf[2][16];
-      float sl[2][16];
-      if (MODE == MODE_STREAMING || diag || kMixed) {
+      if (lam_phase || diag) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
-            const float x = st[kb][j];
             const bool causal = jp <= i_q;
             const bool lam = causal && (jp < a.S || i_q - jp < a.R);
-            if constexpr (MODE == MODE_STREAMING) {
-              sf[kb][j] = lam ? x : -INFINITY;
-            } else {
-              sf[kb][j] = causal ? x : -INFINITY;
-              if constexpr (kMixed) sl[kb][j] = lam ? x : -INFINITY;
-            }
+            sf[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
           }
       } else {
 #pragma unroll
@@ -357,13 +387,6 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       bf16x8 pb[4];
       softmax_update(sf, m_f, l_f, o_f, pb);
       pv(Vt[stage], pb, o_f);
-      if constexpr (kMixed) {
-        if (lam_tile) {
-          bf16x8 pl[4];
-          softmax_update(sl, m_l, l_l, o_l, pl);
-          pv(Vt[stage], pl, o_l);
-        }
-      }
     }
     // the other stage was last read before the previous barrier
     if (more) store_tile(stage ^ 1);
@@ -373,13 +396,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // ---- epilogue -----------------------------------------------------------------
   if (t_q >= a.T) return;
   const float lf = l_f + __shfl_xor(l_f, 32, 64);
-  float wf = 1.0f / lf, wl = 0.0f;
-  if constexpr (kMixed) {
-    const float al = a.alpha[kv];
-    const float ll = l_l + __shfl_xor(l_l, 32, 64);
-    wf = al / lf;
-    wl = (1.0f - al) / ll;
-  }
+  const float wf = alpha / lf;  // alpha = 1 outside the mixed forward
   uint16_t* op = a.out + (((int64_t)b * a.T + t_q) * a.Hq + head) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -389,7 +406,10 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v[r] = o_f[db][4 * jb + r] * wf;
-        if constexpr (kMixed) v[r] = fmaf(o_l[db][4 * jb + r], wl, v[r]);
+        if constexpr (kMixed) {
+          const uint32_t w = lam_pk[db][(4 * jb + r) >> 1];
+          v[r] += __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+        }
       }
       uint2 w;
       w.x = pack_bf16x2(v[0], v[1]);
