@@ -84,7 +84,9 @@ typedef struct {
 /* Byte offsets of the arrays inside the caller-provided buffers.
  * Retrieval buffer, kv_dtype cache:
  *   K  [B][Hr][cap][D] elements at k_offset, V likewise at v_offset, then 32
- *   rows of padding that the decode step may read but never uses.
+ *   rows of padding that the decode step may read but never uses. One head's
+ *   rows plus the padding must stay below 2^31 bytes: (cap + 32) * D * 2 <
+ *   2^31, else DUO_ERR_UNSUPPORTED.
  * Retrieval buffer, INT4_G32 cache (cap32 = capacity rounded up to 32):
  *   K codes [B][Hr][cap32][D/2] bytes at k_offset, token-major: byte b of a
  *   row holds channel 2b in its low nibble and 2b+1 in its high nibble.

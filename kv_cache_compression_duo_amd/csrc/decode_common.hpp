@@ -174,11 +174,14 @@ __device__ __forceinline__ float dot8(const QFrag<G>& q, int g, const u32x4& k) 
 // Tiles are interleaved across the block's waves with the next tile's loads
 // in flight. sscale turns raw dot products into log2-domain scores (softmax
 // scale * log2(e) for bf16 keys, 1 for fp16 keys whose query is pre-scaled).
-// On return l and acc are summed over the wave's rows; m is the wave maximum.
+// slab_bytes is the byte range readable from kc (and from vc): the head's
+// rows plus the padding, below 2^31. On return l and acc are summed over the
+// wave's rows; m is the wave maximum.
 template <int D, int G, typename Tag, int NW>
 __device__ __forceinline__ void attend_cache(WaveState<G>& st, const QFrag<G>& q, float sscale,
                                              const uint16_t* __restrict__ kc,
-                                             const uint16_t* __restrict__ vc, int r0, int r1,
+                                             const uint16_t* __restrict__ vc,
+                                             uint32_t slab_bytes, int r0, int r1,
                                              const uint16_t* knew, const uint16_t* vnew,
                                              bool with_new) {
   constexpr int LPR = D / 8;       // lanes per row
@@ -236,14 +239,21 @@ __device__ __forceinline__ void attend_cache(WaveState<G>& st, const QFrag<G>& q
   };
   int t0 = r0 + wave * kTile;
   if (t0 < r1) {
+    // Buffer loads: the head's rows are one resource (scalar registers), the
+    // lane offset is a constant vector register and the row offset a scalar,
+    // so no per-tile vector address is built (64-bit address temporaries
+    // shared registers with loads in flight and made the loop wait for every
+    // outstanding load).
+    const __amdgpu_buffer_rsrc_t krs = wave_rsrc(kc, slab_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(vc, slab_bytes);
+    const uint32_t loff = (uint32_t)lane * 16u;
     auto load = [&](u32x4 (&kb)[U], u32x4 (&vb)[U], int t) {
       const int tl = t < r1 ? t : r1 - 1;  // wave-uniform
-      const uint16_t* kp = kc + (int64_t)tl * D + lane * 8;
-      const uint16_t* vp = vc + (int64_t)tl * D + lane * 8;
+      const uint32_t soff = (uint32_t)tl * (uint32_t)(D * 2);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        kb[u] = ld16_nt(kp + u * LOAD);
-        vb[u] = ld16_nt(vp + u * LOAD);
+        kb[u] = buf_ld16_nt(krs, loff, soff + u * LOAD * 2);
+        vb[u] = buf_ld16_nt(vrs, loff, soff + u * LOAD * 2);
       }
     };
     auto compute = [&](const u32x4 (&kb)[U], u32x4 (&vb)[U], int t) {

@@ -8,6 +8,10 @@ namespace duo {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8) that waits for all vector memory loads only.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 struct alignas(16) u32x4 {
   uint32_t x, y, z, w;
 };
@@ -24,6 +28,25 @@ typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   v4u32 r = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
   return u32x4{r.x, r.y, r.z, r.w};
+}
+
+// Buffer resource for a wave-uniform byte range [p, p + bytes): the base is
+// moved to scalar registers explicitly (it is uniform by construction), the
+// stride is 0 (raw addressing) and the third dword is the gfx9 default format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte buffer load at byte offset voff (per lane) + soff (scalar), with
+// the non-temporal hint (aux bit 1).
+__device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  typedef uint32_t v4u32b __attribute__((ext_vector_type(4)));
+  const v4u32b x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+  return u32x4{x.x, x.y, x.z, x.w};
 }
 
 // Word i (0..3) and 16-bit half i (0..7) of a 16-byte vector, by value (no

@@ -88,6 +88,11 @@ static duo_status check_desc(const duo_layer_desc* d) {
   if (d->retrieval_dtype == DUO_INT4_G32 &&
       cap32_of(d->retrieval_capacity) * (d->head_dim / 2) >= ((int64_t)1 << 31))
     return DUO_ERR_UNSUPPORTED;
+  // the 16-bit decode kernel reads one head's rows (plus the padding rows)
+  // as one buffer resource with 32-bit byte offsets
+  if (d->retrieval_dtype != DUO_INT4_G32 &&
+      (d->retrieval_capacity + kDecodePadRows) * d->head_dim * 2 >= ((int64_t)1 << 31))
+    return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 

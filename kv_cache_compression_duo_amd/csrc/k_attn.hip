@@ -301,6 +301,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   load_tile(tile_pos(0));
   store_tile(0);
   __syncthreads();
+  // Every load issued so far (the query fragments, tile 0) has landed: say so
+  // explicitly. Without it the wait-count insertion merges the path on which
+  // no tile store waited into the loop header and keeps the query loads
+  // "pending", so each iteration's QK products would wait for the next tile's
+  // prefetch (vmcnt counts in order), exposing its whole latency.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   for (int k = 0; k < ntiles; ++k) {
     const int p0 = tile_pos(k);
     const int stage = k & 1;

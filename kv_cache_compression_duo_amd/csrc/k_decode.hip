@@ -100,8 +100,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 #pragma unroll
       for (int c = 0; c < 8; ++c) qfrag.f[g][c] = qf[g][c];
     }
-    attend_cache<D, G, Tag, NW>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, r0,
-                            has_new ? n : r1, knew, vnew, has_new);
+    const uint32_t slab_bytes = (uint32_t)((a.cap + kDecodePadRows) * D * 2);
+    attend_cache<D, G, Tag, NW>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, slab_bytes,
+                                r0, has_new ? n : r1, knew, vnew, has_new);
     // the new token's cache row (read by no block of this launch)
     if (split == 0 && threadIdx.x < LPR) {
       st16(a.kc + (hb * a.cap + n) * D + threadIdx.x * 8, ld16(knew + threadIdx.x * 8));

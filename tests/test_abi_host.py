@@ -71,6 +71,8 @@ def test_layout_sizes():
     (dict(softmax_scale=-0.1), 1),
     # 4-bit cache: one head's code array must stay below 2^31 bytes
     (dict(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25)), 2),
+    # 16-bit cache: one head's rows plus 32 padding rows must stay below 2^31 bytes
+    (dict(capacity=(1 << 23)), 2),
 ])
 def test_bad_descriptor_rejected(kw, status):
     L = _lib()
@@ -84,6 +86,17 @@ def test_int4_capacity_limit():
     ok = _desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25) - 32)
     assert L.lib.duo_layer_layout(ctypes.byref(ok), ctypes.byref(out)) == 0
     big = _desc(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25) - 31)
+    assert L.lib.duo_layer_layout(ctypes.byref(big), ctypes.byref(out)) == 2
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_capacity_limit(D):
+    L = _lib()
+    out = L.Layout()
+    last = (1 << 31) // (2 * D) - 32 - 1  # (cap + 32) * D * 2 < 2^31
+    ok = _desc(head_dim=D, capacity=last, softmax_scale=D ** -0.5)
+    assert L.lib.duo_layer_layout(ctypes.byref(ok), ctypes.byref(out)) == 0
+    big = _desc(head_dim=D, capacity=last + 1, softmax_scale=D ** -0.5)
     assert L.lib.duo_layer_layout(ctypes.byref(big), ctypes.byref(out)) == 2
 
 
