@@ -49,6 +49,15 @@ __device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t 
   return u32x4{x.x, x.y, x.z, x.w};
 }
 
+// 8-byte variant (two words).
+__device__ __forceinline__ void buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                           uint32_t& w0, uint32_t& w1) {
+  typedef uint32_t v2u32b __attribute__((ext_vector_type(2)));
+  const v2u32b x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2);
+  w0 = x.x;
+  w1 = x.y;
+}
+
 // Word i (0..3) and 16-bit half i (0..7) of a 16-byte vector, by value (no
 // pointer reinterpretation of the struct).
 __device__ __forceinline__ uint32_t word_of(const u32x4& v, int i) {

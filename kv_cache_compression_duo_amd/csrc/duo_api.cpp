@@ -18,12 +18,17 @@ int max_split_for(const duo_layer_desc& d) {
   return (int)(s < 1 ? 1 : s);
 }
 
-// About one retrieval split per compute unit: a streaming read of the cache
-// runs fastest with one 256-thread block per CU, and a CU that gets two
-// blocks while others get one sets the step time. Streaming-head blocks read
-// at most S + R rows, so four of them are counted as one block.
-// DUO_DECODE_SPLIT_TOKENS, if set to a positive value, overrides the rule.
-int decode_split_tokens(const duo_layer* L, int64_t rows, int tile) {
+// Split count: the launch gets at most `blocks` blocks, `blocks` no more
+// than the compute units (a CU that gets two long blocks while others get
+// one sets the step time: 8 blocks more than CUs made a plain read 40 %
+// slower, and 32 splits per head of the Llama-2 layer, 280 blocks, 33 %).
+// The memory-bound 16-bit decode asks for 4/5 of the CUs (measured on the
+// Llama-2 layer: 24 splits per head, 216 blocks, 2.5 % faster than 31); the
+// VALU-bound 4-bit decode asks for all of them (63 splits per head 10 %
+// faster than 48). Streaming-head blocks read at most S + R rows, so four of
+// them are counted as one block. DUO_DECODE_SPLIT_TOKENS, if set to a
+// positive value, overrides the rule.
+int decode_split_tokens(const duo_layer* L, int64_t rows, int tile, int blocks) {
   static int env = -1;
   if (env < 0) {
     const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
@@ -33,7 +38,7 @@ int decode_split_tokens(const duo_layer* L, int64_t rows, int tile) {
   int64_t st = env;
   if (st <= 0) {
     const int B = L->d.batch;
-    int64_t per_head = (int64_t)(L->cus - (B * L->Hs) / 4) / ((int64_t)B * (L->Hr > 0 ? L->Hr : 1));
+    int64_t per_head = (int64_t)(blocks - (B * L->Hs) / 4) / ((int64_t)B * (L->Hr > 0 ? L->Hr : 1));
     if (per_head < 1) per_head = 1;
     st = (rows + per_head - 1) / per_head;
   }

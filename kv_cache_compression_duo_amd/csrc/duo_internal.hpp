@@ -40,7 +40,7 @@ size_t ws_bytes(const duo_layer_desc& d, int max_split);
 int max_split_for(const duo_layer_desc& d);
 // Split-K range (tokens, a multiple of `tile`, at least kMinSplitTokens) of a
 // decode step over `rows` cache rows.
-int decode_split_tokens(const duo_layer* L, int64_t rows, int tile);
+int decode_split_tokens(const duo_layer* L, int64_t rows, int tile, int blocks);
 
 // ---- launchers (return hipSuccess or the launch error) ----------------------
 hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v, int T,

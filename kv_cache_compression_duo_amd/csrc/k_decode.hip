@@ -215,7 +215,7 @@ hipError_t launch_decode(const duo_layer* L, const void* q, const void* k_new,
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;
   const int B = d.batch;
-  const int st = decode_split_tokens(L, rows, 1);
+  const int st = decode_split_tokens(L, rows, 1, L->cus * 4 / 5);
   const int ms = L->max_split;
   if (d.head_dim == 128) {
     if (d.kv_dtype == DUO_FP16) return launch_g<128, Fp16Tag>(L->G, a, B, rows, st, ms, s);

@@ -129,36 +129,40 @@ struct I4Tile {
   u32x4 ks[2], vs[2];
 };
 
-// Offsets are 32-bit from per-head bases (the layout check bounds a head's
-// code and scale arrays below 2^31 bytes), so the loads take a uniform base.
+// Where one head's arrays are read from: one buffer resource per array (the
+// layout check bounds a head's code and scale arrays below 2^31 bytes, so
+// 32-bit offsets reach all of them) and this lane's constant byte offsets.
+// A tile's own offset is a scalar, so no per-tile vector address is built.
+struct I4Src {
+  __amdgpu_buffer_rsrc_t k, v, ks, vs;
+  uint32_t klane, vlane, slane;
+};
+
 template <int D>
-__device__ __forceinline__ void load_tile(I4Tile<D>& T, const uint8_t* __restrict__ kc,
-                                          const uint8_t* __restrict__ vc,
-                                          const uint32_t* __restrict__ ks,
-                                          const uint32_t* __restrict__ vs, int t0, int n16,
-                                          int q4, int gc) {
+__device__ __forceinline__ void load_tile(I4Tile<D>& T, const I4Src& S, int t0) {
   constexpr int NG = D / 32;
   const uint32_t t = (uint32_t)t0;
+  // key rows t + 16 hf + n16, bytes q4 * D/8 .. + D/8 of the row
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const uint8_t* p = kc + ((t + 16 * hf + n16) * (D / 2) + q4 * (D / 8));
+    const uint32_t so = (t + 16 * hf) * (D / 2);
     if constexpr (D == 128) {
-      const u32x4 w = ld16_nt(p);
+      const u32x4 w = buf_ld16_nt(S.k, S.klane, so);
       T.k[hf][0] = w.x; T.k[hf][1] = w.y; T.k[hf][2] = w.z; T.k[hf][3] = w.w;
     } else {
-      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-      T.k[hf][0] = w.x; T.k[hf][1] = w.y;
+      buf_ld8_nt(S.k, S.klane, so, T.k[hf][0], T.k[hf][1]);
     }
   }
+  // value block t/32: 16-byte piece (c4 * 16 + n16) * 4 + q4
   const uint32_t blk = t >> 5;
 #pragma unroll
   for (int c4 = 0; c4 < I4Tile<D>::NC; ++c4)
-    T.v[c4] = ld16_nt(vc + (blk * 16 * D + ((c4 * 16 + n16) * 4 + q4) * 16));
-  const uint32_t sw = (blk * NG + gc) * 32 + 4 * q4;
+    T.v[c4] = buf_ld16_nt(S.v, S.vlane, blk * 16 * D + c4 * 1024);
+  // scale/zero words (blk * NG + gc) * 32 + 4 q4 + 16 hf .. + 3
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    T.ks[hf] = ld16_nt(ks + (sw + 16 * hf));
-    T.vs[hf] = ld16_nt(vs + (sw + 16 * hf));
+    T.ks[hf] = buf_ld16_nt(S.ks, S.slane, blk * NG * 128 + 64 * hf);
+    T.vs[hf] = buf_ld16_nt(S.vs, S.slane, blk * NG * 128 + 64 * hf);
   }
 }
 
@@ -263,10 +267,18 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   const float qoff = -128.0f * qsum;
   const float qscale = a.qscale;
 
-  const uint8_t* kc = a.kcodes + hb * a.cap32 * (D / 2);
-  const uint8_t* vc = a.vcodes + hb * a.cap32 * (D / 2);
-  const uint32_t* ks = a.ksz + hb * a.cap32 * NG;
-  const uint32_t* vs = a.vsz + hb * a.cap32 * NG;
+  I4Src src;
+  {
+    const uint32_t code_bytes = (uint32_t)(a.cap32 * (D / 2));
+    const uint32_t sz_bytes = (uint32_t)(a.cap32 * NG * 4);
+    src.k = wave_rsrc(a.kcodes + hb * a.cap32 * (D / 2), code_bytes);
+    src.v = wave_rsrc(a.vcodes + hb * a.cap32 * (D / 2), code_bytes);
+    src.ks = wave_rsrc(a.ksz + hb * a.cap32 * NG, sz_bytes);
+    src.vs = wave_rsrc(a.vsz + hb * a.cap32 * NG, sz_bytes);
+    src.klane = (uint32_t)(n16 * (D / 2) + q4 * (D / 8));
+    src.vlane = (uint32_t)((n16 * 4 + q4) * 16);
+    src.slane = (uint32_t)((gc * 32 + 4 * q4) * 4);
+  }
 
   float m_run = -INFINITY, l_run = 0.0f, zacc = 0.0f;
   f32x4 o[NB];
@@ -366,18 +378,18 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   int t0 = r0 + wave * 32;
   if (t0 < r1) {
     I4Tile<D> ta, tb;
-    load_tile<D>(ta, kc, vc, ks, vs, t0, n16, q4, gc);
+    load_tile<D>(ta, src, t0);
     auto step = [&](const I4Tile<D>& T, int t) {
       if (t + 32 <= r1) compute(T, t, BoolC<true>{});
       else compute(T, t, BoolC<false>{});
     };
     for (;;) {
       const int t1 = t0 + stride;
-      load_tile<D>(tb, kc, vc, ks, vs, clamp(t1), n16, q4, gc);
+      load_tile<D>(tb, src, clamp(t1));
       step(ta, t0);
       if (t1 >= r1) break;
       t0 = t1 + stride;
-      load_tile<D>(ta, kc, vc, ks, vs, clamp(t0), n16, q4, gc);
+      load_tile<D>(ta, src, clamp(t0));
       step(tb, t1);
       if (t0 >= r1) break;
     }
@@ -514,7 +526,7 @@ hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_n
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;
   const int B = d.batch;
-  const int st = decode_split_tokens(L, rows, 32);
+  const int st = decode_split_tokens(L, rows, 32, L->cus);
   const int ms = L->max_split;
   if (d.head_dim == 128) {
     if (d.kv_dtype == DUO_FP16) return launch_i4_g<128, Fp16Tag>(L->G, a, B, rows, st, ms, s);
