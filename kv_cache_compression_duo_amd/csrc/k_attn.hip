@@ -42,6 +42,7 @@
 namespace duo {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { MODE_RETRIEVAL = 0, MODE_STREAMING = 1, MODE_MIXED = 2 };
@@ -236,10 +237,13 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 
   // One online-softmax update of (m, l, O) from masked raw scores (m in raw
   // score units; the scale, folded with log2(e), enters the exp2 argument as
-  // one FMA). O and l are rescaled only when some lane's maximum grew
-  // (wave-uniform test); returns P packed as the B operands of the four
-  // 16-key slices.
+  // one FMA). m is a reference maximum, not necessarily the exact one: O and
+  // l are rescaled only when some lane's tile maximum exceeds its m by more
+  // than 8 in the log2 domain (wave-uniform test), so P stays at most 2^8 and
+  // O / l is unchanged; most tiles skip the rescale. Returns P packed as the
+  // B operands of the four 16-key slices.
   const float c2 = a.scale_log2;
+  const float lazy = 8.0f / c2;  // raw-score growth that forces a rescale
   auto softmax_update = [&](const float (&sc)[2][16], float& m, float& l, f32x16 (&O)[DB],
                             bf16x8 (&pb)[4]) {
     float tm = -INFINITY;
@@ -249,28 +253,38 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sc[kb][j]);
     tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
     const float mn = fmaxf(m, tm);
-    if (__ballot(mn > m) != 0) {
-      const float corr = fast_exp2((m - mn) * c2);  // m = -inf -> 0 (mn is finite here)
+    // m = -inf (no allowed key yet) and a finite tm always rescales
+    if (__ballot(tm > m + lazy) != 0) {
+      // m = -inf, mn finite -> 0; a lane still without an allowed key (both
+      // -inf, l = 0 and O = 0) keeps factor 1 instead of exp2(NaN)
+      const float corr = mn == -INFINITY ? 1.0f : fast_exp2((m - mn) * c2);
       l *= corr;
 #pragma unroll
       for (int db = 0; db < DB; ++db) O[db] *= corr;
       m = mn;
     }
     const float mc = m == -INFINITY ? 0.0f : m * c2;  // no allowed key yet: p = 0
-    float ls = 0.0f;
     float p[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        p[kb][j] = fast_exp2(fmaf(sc[kb][j], c2, -mc));
-        ls += p[kb][j];
-      }
-    l += ls;
+      for (int j = 0; j < 16; ++j) p[kb][j] = fast_exp2(fmaf(sc[kb][j], c2, -mc));
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)p[s >> 1][8 * (s & 1) + i];
+    // the row sum adds the bf16 values the PV product uses, two per dot2
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[s][i], pb[s][i + 1]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[s][i + 2], pb[s][i + 3]}, ones, ls1,
+                                              false);
+      }
+    l += ls0 + ls1;
   };
   auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
     // all V^T fragments of two 16-key slices are requested before their

@@ -70,3 +70,14 @@ def test_mixed_shapes(G, D, T):
     say(f"case: mixed G={G} D={D} T={T}")
     inp = make_inputs(w, tokens=T, seed=9400 + T)
     _mixed(inp, inp.alpha, label=f"G{G}D{D}T{T}")
+
+
+@pytest.mark.parametrize("S,R", [(0, 1), (0, 5), (3, 7)])
+def test_mixed_short_window_no_sink(S, R):
+    # no sink tokens / short windows: Lambda-phase rows of a block's later
+    # waves have no allowed key in its first visited tile
+    w = dataclasses.replace(WORKLOADS["llama2_7b_mixed_16k"], n_q_heads=4, n_kv_heads=4, sink=S,
+                            recent=R)
+    say(f"case: mixed S={S} R={R} T=200")
+    inp = make_inputs(w, tokens=200, seed=9600 + 10 * S + R)
+    _mixed(inp, inp.alpha, label=f"S{S}R{R}")

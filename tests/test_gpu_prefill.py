@@ -107,6 +107,17 @@ def test_prefill_around_sink_and_window(T):
     _run_prefill(inp, [T], decode_steps=3, label=f"T{T}")
 
 
+@pytest.mark.parametrize("S,R", [(0, 5), (0, 9), (3, 7)])
+def test_prefill_short_window_no_sink(S, R):
+    # without sink tokens a block's first Lambda tile is a window tile, and
+    # rows of its later waves have no key in it
+    w = dataclasses.replace(WORKLOADS["mha8_d64_seq1024"], n_q_heads=4, n_kv_heads=4,
+                            fixed_retrieval=(2,), sink=S, recent=R)
+    say(f"case: S={S} R={R}, chunks 130/170, then 2 decode steps")
+    inp = make_inputs(w, tokens=300, steps=2, seed=7100 + 10 * S + R)
+    _run_prefill(inp, [130, 170], decode_steps=2, label=f"S{S}R{R}")
+
+
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (4, 64), (8, 128)])
 def test_prefill_group_sizes(G, D):
     w = dataclasses.replace(WORKLOADS["llama3_8b_prefill_64k"], n_q_heads=2 * G, n_kv_heads=2,
