@@ -30,6 +30,19 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return u32x4{r.x, r.y, r.z, r.w};
 }
 
+// A wave-uniform pointer to global memory moved to scalar registers
+// explicitly; it is rebuilt as a global-address-space pointer, so loads
+// through it stay global (not flat) loads.
+template <typename T>
+__device__ __forceinline__ T* wave_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  typedef __attribute__((address_space(1))) T global_t;
+  global_t* g = (global_t*)(((uint64_t)hi << 32) | lo);
+  return (T*)g;
+}
+
 // Buffer resource for a wave-uniform byte range [p, p + bytes): the base is
 // moved to scalar registers explicitly (it is uniform by construction), the
 // stride is 0 (raw addressing) and the third dword is the gfx9 default format.

@@ -100,16 +100,27 @@ struct KeySrc {
       const uint16_t* base = v ? a.v_in : a.k_in;
       return base + (((int64_t)b * a.T + pc) * a.Hkv + kv) * D;
     } else {
-      const uint16_t* in = v ? a.v_in : a.k_in;
-      if (p >= a.n && p < a.n + a.T)
-        return in + (((int64_t)b * a.T + (p - a.n)) * a.Hkv + kv) * D;
+      // Three sources: the chunk itself, the ring (sink slots, then the
+      // recent window), and a fixed chunk row for positions no query of the
+      // launch may attend. All three are computed and one is selected, with
+      // no per-lane branch. A window position p (n - R <= p < n) has ring
+      // slot S + (p - S) mod R = S + (c0 + R + p - n) mod R with the uniform
+      // c0 = (n - S) mod R, and c0 + R + p - n lies in [c0, c0 + R): one
+      // conditional subtract instead of a per-lane division.
+      const bool chunk = p >= a.n && p < a.n + a.T;
       const int rlo = a.n - a.R > a.S ? a.n - a.R : a.S;
-      if (p >= 0 && p < a.n && (p < a.S || p >= rlo)) {
-        const int slot = p < a.S ? p : a.S + (p - a.S) % a.R;
-        const uint16_t* ring = v ? a.vr : a.kr;
-        return ring + (((int64_t)b * a.Hs + (kv - a.Hr)) * (a.S + a.R) + slot) * D;
-      }
-      return in + ((int64_t)b * a.T * a.Hkv + kv) * D;  // masked for every query
+      const bool ring = !chunk && p >= 0 && p < a.n && (p < a.S || p >= rlo);
+      const int c0 = (int)((uint32_t)(a.n > a.S ? a.n - a.S : 0) % (uint32_t)a.R);
+      const int q = c0 + a.R + (p - a.n);
+      const int slot = p < a.S ? p : a.S + (q >= a.R ? q - a.R : q);
+      const int64_t i_chunk = ((int64_t)b * a.T + (p - a.n)) * a.Hkv + kv;
+      const int64_t i_ring = ((int64_t)b * a.Hs + (kv - a.Hr)) * (a.S + a.R) + slot;
+      const int64_t i_mask = (int64_t)b * a.T * a.Hkv + kv;
+      // both bases in scalar registers, so the per-lane choice is a register
+      // select (not a load of the chosen pointer from the argument block)
+      const uint16_t* ring_base = wave_ptr(v ? a.vr : a.kr);
+      const uint16_t* in_base = wave_ptr(v ? a.v_in : a.k_in);
+      return (ring ? ring_base : in_base) + (chunk ? i_chunk : ring ? i_ring : i_mask) * D;
     }
   }
 };
@@ -394,8 +405,9 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
+            // bitwise operators: a select per element, no per-lane branches
             const bool causal = jp <= i_q;
-            const bool lam = causal && (jp < a.S || i_q - jp < a.R);
+            const bool lam = causal & ((jp < a.S) | (i_q - jp < a.R));
             sf[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
           }
       } else {
