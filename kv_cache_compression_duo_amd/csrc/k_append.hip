@@ -11,6 +11,7 @@
 // division so that the codes are reproducible bit for bit.
 #include "device_common.hpp"
 #include "duo_internal.hpp"
+#include "int4_codec.hpp"
 
 namespace duo {
 
@@ -32,42 +33,6 @@ __global__ void append_rows_kernel(const u32x4* __restrict__ k, const u32x4* __r
   int64_t dst = (((int64_t)b * Hr + h) * cap + n + t) * chunks + c;
   kc[dst] = k[src];
   vc[dst] = v[src];
-}
-
-// ---- 4-bit group encoding --------------------------------------------------
-template <typename Tag>
-__device__ __forceinline__ void encode_group_part(const u32x4& raw, uint32_t* codes_out,
-                                                  uint32_t* sz_out) {
-  // Four consecutive lanes hold one 32-channel group, 8 channels each.
-  float x[8];
-  unpack8<Tag>(raw, x);
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    mn = fminf(mn, x[j]);
-    mx = fmaxf(mx, x[j]);
-  }
-  // min / max over the 4 lanes of the group (quad_perm butterflies)
-  mn = fminf(mn, dpp<0xB1>(mn));
-  mx = fmaxf(mx, dpp<0xB1>(mx));
-  mn = fminf(mn, dpp<0x4E>(mn));
-  mx = fmaxf(mx, dpp<0x4E>(mx));
-  _Float16 s16 = (_Float16)__fdiv_rn(mx - mn, 15.0f);
-  _Float16 z16 = (_Float16)mn;
-  float s = (float)s16, z = (float)z16;
-  uint32_t packed = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float c = 0.0f;
-    if (s != 0.0f) {
-      c = rintf(__fdiv_rn(x[j] - z, s));
-      c = fminf(fmaxf(c, 0.0f), 15.0f);
-    }
-    packed |= ((uint32_t)c & 0xFu) << (4 * j);
-  }
-  *codes_out = packed;
-  *sz_out = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
 }
 
 // 4-bit cache append. Key codes are token-major ([cap32][D/2] bytes, byte b of

@@ -40,6 +40,7 @@
 //   * the running maximum is rescaled only when some lane's maximum grows.
 #include "decode_common.hpp"
 #include "duo_internal.hpp"
+#include "int4_codec.hpp"
 #include "split_merge.hpp"
 
 namespace duo {
@@ -54,10 +55,10 @@ struct Int4DecodeArgs {
   const uint16_t* k_new;   // [B][Hkv][D] ring dtype
   const uint16_t* v_new;
   uint16_t* out;           // [B][Hq][D] bf16
-  const uint8_t* kcodes;   // [B][Hr][cap32][D/2] bytes
-  const uint8_t* vcodes;   // [B][Hr][cap32/32][16 D] bytes
-  const uint32_t* ksz;     // [B][Hr][cap32/32][D/32][32] (fp16 s | fp16 z << 16)
-  const uint32_t* vsz;
+  uint8_t* kcodes;         // [B][Hr][cap32][D/2] bytes
+  uint8_t* vcodes;         // [B][Hr][cap32/32][16 D] bytes
+  uint32_t* ksz;           // [B][Hr][cap32/32][D/32][32] (fp16 s | fp16 z << 16)
+  uint32_t* vsz;
   uint16_t* kr;            // ring [B][Hs][S+R][D]
   uint16_t* vr;
   uint32_t* counters;
@@ -65,7 +66,7 @@ struct Int4DecodeArgs {
   float* acc;
   int Hq, Hkv, Hr, Hs, S, R, max_split;
   int64_t cap32;
-  int n;                   // position of the new token (already in the 4-bit cache)
+  int n;                   // position of the new token (quantised into the cache here)
   int n_split, split_tokens;
   float qscale;            // softmax scale * log2(e)
 };
@@ -229,7 +230,11 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   // ---------------------------------------------------------------- retrieval
   const int split = rb % a.n_split;
   const int r0 = split * a.split_tokens;
-  const int r1 = r0 + a.split_tokens < a.n + 1 ? r0 + a.split_tokens : a.n + 1;
+  const int r_end = r0 + a.split_tokens < a.n + 1 ? r0 + a.split_tokens : a.n + 1;
+  // the split holding position n also takes the new token, which it quantises
+  // itself (below); its cache rows end at n
+  const bool has_new = r_end == a.n + 1;
+  const int r1 = has_new ? a.n : r_end;
   const int64_t hb = (int64_t)b * a.Hr + kvh;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int hc = n16 / NG, gc = n16 % NG;  // this lane's (head, group) column
@@ -395,6 +400,76 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
     }
   }
 
+  // ---- the new token ---------------------------------------------------------
+  // Quantised here exactly as the append kernel does (lanes 0..D/8-1 of wave 0
+  // encode K, lanes 32.. encode V, 8 channels each, quads = 32-channel
+  // groups); its codes and scale/zero words are written for later steps. No
+  // block of this launch reads row n as data: the 32-token tile holding it
+  // belongs to this split only and is masked past the cache rows, and the one
+  // value-code byte it shares with token n - 16 keeps that token's nibble.
+  // It enters the block merge from its dequantised values fma(c, s, z) as one
+  // more entry: score q . k^ per head, weight 1, values v^.
+  __shared__ float new_m[G];
+  __shared__ float new_acc[G][D];
+  if (has_new && wave == 0) {
+    constexpr int CH = D / 8;  // 8-channel chunks of a row
+    const bool vside = lane >= 32;
+    const bool act = (lane & 31) < CH;
+    const int c = act ? (lane & 31) : 0;  // idle quads duplicate chunks 0..3
+    const uint16_t* src = (vside ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + kvh) * D + 8 * c;
+    uint32_t codes, sz;
+    encode_group_part<RingTag>(ld16(src), &codes, &sz);
+    const int n = a.n;
+    if (act) {
+      const int64_t w = ((hb * (a.cap32 / 32) + n / 32) * NG + c / 4) * 32 + n % 32;
+      if (!vside) {
+        reinterpret_cast<uint32_t*>(a.kcodes)[(hb * a.cap32 + n) * CH + c] = codes;
+        if ((c & 3) == 0) a.ksz[w] = sz;
+      } else {
+        if ((c & 3) == 0) a.vsz[w] = sz;
+        // token n is nibble n / 16 % 2 of byte position n % 16 of its block
+        const int m16 = n % 16;
+        const bool hi = (n % 32) >= 16;
+        uint8_t* vb = a.vcodes + (hb * (a.cap32 / 32) + n / 32) * 16 * D +
+                      16 * (4 * (16 * (c / 8) + 8 * (c % 2)) + m16 / 4) + 4 * ((c % 8) / 2) +
+                      m16 % 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint8_t* dst = vb + 64 * j;
+          const uint32_t nib = (codes >> (4 * j)) & 0xFu;
+          const uint32_t old = *dst;
+          *dst = (uint8_t)(hi ? (old & 0x0Fu) | (nib << 4) : (old & 0xF0u) | nib);
+        }
+      }
+    }
+    float xh[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xh[j] = decode_code(codes, sz, j);
+    // per-head dot q . k^ over the K lanes (lanes 0..31; others add 0)
+    float dots[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float qv[8];
+      unpack8<Bf16Tag>(ld16(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + 8 * c), qv);
+      float d = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d = fmaf(qv[j], xh[j], d);
+      dots[g] = (!vside && act) ? d : 0.0f;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) dots[g] += __shfl_xor(dots[g], off, 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) new_m[g] = dots[g] * a.qscale;  // log2 units
+    }
+    if (vside && act) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) new_acc[g][8 * c + j] = xh[j];
+    }
+  }
+
   // ---- wave totals -> LDS --------------------------------------------------
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -425,9 +500,11 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
     const int g = threadIdx.x;
     float M = red.m[0][g];
     for (int w = 1; w < NW; ++w) M = fmaxf(M, red.m[w][g]);
+    if (has_new) M = fmaxf(M, new_m[g]);
     float Lsum = 0.0f;
     for (int w = 0; w < NW; ++w)
       Lsum += red.m[w][g] == -INFINITY ? 0.0f : red.l[w][g] * fast_exp2(red.m[w][g] - M);
+    if (has_new) Lsum += fast_exp2(new_m[g] - M);
     red.M[g] = M;
     red.L[g] = Lsum;
   }
@@ -437,6 +514,7 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
     float s = 0.0f;
     for (int w = 0; w < NW; ++w)
       if (red.m[w][g] != -INFINITY) s += red.acc[w][g][dd] * fast_exp2(red.m[w][g] - red.M[g]);
+    if (has_new) s += new_acc[g][dd] * fast_exp2(new_m[g] - red.M[g]);
     red.acc[0][g][dd] = s;  // each (g, dd) is read and written by one thread only
   }
   __syncthreads();
@@ -496,19 +574,18 @@ static hipError_t launch_i4_g(int G, const Int4DecodeArgs& a, int B, int64_t row
 hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_new,
                               const void* v_new, void* out, hipStream_t s) {
   const duo_layer_desc& d = L->d;
-  // the new token goes into the 4-bit cache first (append, then attend)
-  hipError_t e = launch_append_cache(L, k_new, v_new, 1, s);
-  if (e != hipSuccess) return e;
+  // one launch: the block whose split holds position n quantises the new
+  // token into the 4-bit cache and attends to it
   Int4DecodeArgs a;
   WsView ws = ws_view(L);
   a.q = static_cast<const uint16_t*>(q);
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.out = static_cast<uint16_t*>(out);
-  a.kcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.k_offset);
-  a.vcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.v_offset);
-  a.ksz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.k_sz_offset);
-  a.vsz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.v_sz_offset);
+  a.kcodes = reinterpret_cast<uint8_t*>(L->rbuf + L->lay.k_offset);
+  a.vcodes = reinterpret_cast<uint8_t*>(L->rbuf + L->lay.v_offset);
+  a.ksz = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.k_sz_offset);
+  a.vsz = reinterpret_cast<uint32_t*>(L->rbuf + L->lay.v_sz_offset);
   a.kr = reinterpret_cast<uint16_t*>(L->sbuf + L->lay.ring_k_offset);
   a.vr = reinterpret_cast<uint16_t*>(L->sbuf + L->lay.ring_v_offset);
   a.counters = ws.counters;

@@ -77,6 +77,43 @@ def test_int4_append_codes_bit_exact(kv_dtype, D):
     say(f"  {kv_dtype} D={D}: {n} tokens of K/V codes, scales and zero-points bit-exact")
 
 
+@pytest.mark.parametrize("kv_dtype,D", [("fp16", 128), ("bf16", 128), ("fp16", 64)])
+def test_int4_decode_writes_codes_bit_exact(kv_dtype, D):
+    # the decode step quantises its new token into the 4-bit cache itself:
+    # after steps that cross both nibble halves and a 32-token block boundary
+    # every row's codes, scales and zero-points equal the oracle's
+    Hq, Hkv, ctx, steps = 8, 2, 45, 40
+    say(f"case: {kv_dtype} D={D}, context {ctx} then {steps} decode steps, codes checked")
+    g = rng(510 + D)
+    n = ctx + steps
+    k = normal(g, (n, Hkv, D)) * 2.0
+    v = normal(g, (n, Hkv, D))
+    q = normal(g, (steps, Hq, D))
+    rnd = round_fp16 if kv_dtype == "fp16" else (lambda x: torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+    k, v = rnd(k), rnd(v)
+    tdt = torch.float16 if kv_dtype == "fp16" else torch.bfloat16
+    lay = _int4_layer(Hq, Hkv, D, 1, n, D ** -0.5, kv_dtype=kv_dtype)
+    lay.append_kv(to_dev(k[:ctx], tdt)[None], to_dev(v[:ctx], tdt)[None])
+    for s in range(steps):
+        p = ctx + s
+        lay.decode(to_dev(q[s])[None, None], to_dev(k[p], tdt)[None, None],
+                   to_dev(v[p], tdt)[None, None])
+    torch.cuda.synchronize()
+    assert lay.n_tokens == n
+    K, V, KS, VS = lay.retrieval_int4()
+    ck, sk, zk = oracle.quantize_int4_g32(k[:, 0])
+    cv, sv, zv = oracle.quantize_int4_g32(v[:, 0])
+    np.testing.assert_array_equal(K[0, 0, :n].cpu().numpy(), oracle.pack_nibbles(ck))
+    np.testing.assert_array_equal(_v_codes_per_token(V[0, 0], n, D), cv)
+    ks = _sz_per_token(KS[0, 0], n)
+    vs = _sz_per_token(VS[0, 0], n)
+    np.testing.assert_array_equal(ks[..., 0].view(np.uint16), sk.view(np.uint16))
+    np.testing.assert_array_equal(ks[..., 1].view(np.uint16), zk.view(np.uint16))
+    np.testing.assert_array_equal(vs[..., 0].view(np.uint16), sv.view(np.uint16))
+    np.testing.assert_array_equal(vs[..., 1].view(np.uint16), zv.view(np.uint16))
+    say(f"  {n} rows of codes, scales and zero-points bit-exact after {steps} decode steps")
+
+
 def _run_int4_decode(inp, context, steps, *, kv_dtype="fp16", label=""):
     w = inp.workload
     Hq, Hkv, D = inp.q_steps.shape[1], w.n_kv_heads, w.head_dim
