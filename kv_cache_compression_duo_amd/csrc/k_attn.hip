@@ -237,13 +237,20 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 
   // ---- state --------------------------------------------------------------------
   // One softmax state (m, l, O). The mixed forward runs its Lambda phase in
-  // it, folds (1 - alpha) * O / l into lam_pk (bf16 pairs) and restarts it for
-  // the causal phase, so it never holds two sets of accumulators.
+  // it, folds (1 - alpha) * O / l into bf16 pairs and restarts it for the
+  // causal phase, so it never holds two sets of accumulators. The folded
+  // pairs are parked in LDS until the epilogue (each lane reads back only what
+  // it wrote), which leaves the causal loop the registers the plain prefill
+  // loop has (held in registers they made the compiler fetch the K fragments
+  // two at a time, each pair of products waiting on its LDS read).
   f32x16 o_f[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
   float m_f = -INFINITY, l_f = 0.0f;
-  uint32_t lam_pk[kMixed ? DB : 1][8];
+  __shared__ uint32_t lam_lds[kMixed ? NW * DB * 8 * 64 : 1];
+  auto lam_at = [&](int db, int i) -> uint32_t& {
+    return lam_lds[((wave * DB + db) * 8 + i) * 64 + lane];
+  };
   const float alpha = kMixed ? a.alpha[kv] : 1.0f;
 
   // One online-softmax update of (m, l, O) from masked raw scores (m in raw
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          lam_pk[db][i] = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
+          lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
         o_f[db] = f32x16{};
       }
       m_f = -INFINITY;
@@ -361,36 +368,19 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     {
       const uint16_t* krow0 = Ks[stage] + q32 * KPAD + 8 * h2;
       const uint16_t* krow1 = krow0 + 32 * KPAD;
-      if constexpr (!kMixed) {
-        bf16x8 ak0[KS], ak1[KS];
+      bf16x8 ak0[KS], ak1[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
-        asm volatile("" ::: "memory");
+      for (int ks = 0; ks < KS; ++ks)
+        ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
+      asm volatile("" ::: "memory");
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
-        asm volatile("" ::: "memory");
+      for (int ks = 0; ks < KS; ++ks)
+        ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
+      asm volatile("" ::: "memory");
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
-          st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
-        }
-      } else {
-        // the mixed forward also holds its Lambda result: one 32-key block's
-        // fragments at a time
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint16_t* krow = kb ? krow1 : krow0;
-          bf16x8 ak[KS];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ks));
-          asm volatile("" ::: "memory");
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qf[ks], st[kb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
+        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
       }
     }
     // raw scores with this mode's mask; tiles wholly below the wave's first
@@ -439,7 +429,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int r = 0; r < 4; ++r) {
         v[r] = o_f[db][4 * jb + r] * wf;
         if constexpr (kMixed) {
-          const uint32_t w = lam_pk[db][(4 * jb + r) >> 1];
+          const uint32_t w = lam_at(db, (4 * jb + r) >> 1);
           v[r] += __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
         }
       }
