@@ -62,6 +62,7 @@ struct AttnArgs {
   int n;         // absolute position of token 0 of the chunk (0 for mixed)
   int n_qtiles;  // query token tiles
   int kv_base;   // first KV head handled by the launch
+  int tiles_in_y;  // grid (head groups, query tiles) rather than (query tiles, head groups)
   float scale_log2;
 };
 
@@ -150,9 +151,15 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const int h2 = lane >> 5, q32 = lane & 31;
   const int b = blockIdx.z;
   const int groups = a.G / HB;
-  const int kv = a.kv_base + (int)blockIdx.y / groups;
-  const int head = kv * a.G + ((int)blockIdx.y % groups) * HB + (wave % HB);
-  const int tile = a.n_qtiles - 1 - (int)blockIdx.x;  // longest rows first
+  // Blocks are dispatched in linear order, x fastest. With query tiles in y
+  // the longest rows of every head come first (global longest-first order,
+  // no late long blocks) and block i of a row lands on XCD i mod 8, so an XCD
+  // sees only some heads' keys and values (L2 reuse).
+  const int hg = (int)(a.tiles_in_y ? blockIdx.x : blockIdx.y);  // head group
+  const int tq = (int)(a.tiles_in_y ? blockIdx.y : blockIdx.x);
+  const int kv = a.kv_base + hg / groups;
+  const int head = kv * a.G + (hg % groups) * HB + (wave % HB);
+  const int tile = a.n_qtiles - 1 - tq;  // longest rows first
   const int tok0 = tile * BMT;
   const int t_q = tok0 + (wave / HB) * TOKW + q32;   // this lane's query token
   const int t_qc = t_q < a.T ? t_q : a.T - 1;
@@ -447,7 +454,10 @@ static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
   constexpr int BMT = 32 * NW / HB;
   AttnArgs x = a;
   x.n_qtiles = (a.T + BMT - 1) / BMT;
-  dim3 grid((unsigned)x.n_qtiles, (unsigned)(n_kv * (a.G / HB)), (unsigned)B);
+  const unsigned hgs = (unsigned)(n_kv * (a.G / HB));
+  x.tiles_in_y = x.n_qtiles <= 65535;  // the y extent of a grid is 16 bits
+  dim3 grid(x.tiles_in_y ? hgs : (unsigned)x.n_qtiles, x.tiles_in_y ? (unsigned)x.n_qtiles : hgs,
+            (unsigned)B);
   attn_kernel<D, HB, MODE><<<grid, 64 * NW, 0, s>>>(x);
   return hipGetLastError();
 }
