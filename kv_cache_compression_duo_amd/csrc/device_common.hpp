@@ -62,6 +62,13 @@ __device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t 
   return u32x4{x.x, x.y, x.z, x.w};
 }
 
+// 16-byte buffer load with default caching.
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v4u32b __attribute__((ext_vector_type(4)));
+  const v4u32b x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return u32x4{x.x, x.y, x.z, x.w};
+}
+
 // 8-byte variant (two words).
 __device__ __forceinline__ void buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                            uint32_t& w0, uint32_t& w1) {

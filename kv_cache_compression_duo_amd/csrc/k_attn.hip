@@ -74,13 +74,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
 
 // Position (in 8-byte units) of the 4-key chunk c of V^T row d in LDS. Chunks
 // are stored in pairs {4s + j, 4s + j + 2} (j = 0, 1), the two chunks one lane
-// of the PV product reads, so they come back in one ds_read_b128; pair slots
-// are XOR-swizzled by d so that 8 consecutive rows hit distinct banks.
+// of the PV product reads, so they come back in one ds_read_b128. A 128-byte
+// row covers half of the 64 LDS banks and a 16-byte read is served 16 lanes
+// (16 consecutive rows) at a time, so pair slots are XOR-swizzled by d / 2:
+// the 8 even and the 8 odd rows of a group each take 8 distinct slots
+// (swizzling by d, rows d and d + 8 met in the same banks: counters showed a
+// third of the LDS cycles stalled on bank conflicts).
 __device__ __forceinline__ int vt_slot(int c, int d) {
   const int s4 = c >> 2, j = c & 3;              // c = 4*s4 + j
   const int pair = 2 * s4 + (j & 1);            // {4s+0, 4s+2} -> 2s, {4s+1, 4s+3} -> 2s+1
   const int half = j >> 1;                      // first or second chunk of the pair
-  return (((pair ^ (d & 7)) << 1) | half);
+  return (((pair ^ ((d >> 1) & 7)) << 1) | half);
 }
 
 template <int D>
@@ -199,47 +203,80 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   }
 
   // ---- global -> register staging of one K/V tile ------------------------------
-  // 256 threads stage K and 256 stage V (one set of 256 does both when the
-  // block has 4 waves); the roles are wave-uniform.
-  constexpr bool kSplitStage = NW == 8;
+  // 256 threads stage K and 256 stage V; the roles are wave-uniform.
+  // Retrieval mode reads the head's cached rows as one buffer resource (rows
+  // at or past the chunk's end read as zeros; the causal mask removes them),
+  // so a tile's addresses are one add per lane (53 fewer VALU per tile than
+  // per-row pointers), and both roles load into one set of registers (the
+  // 128-bit buffer loads keep their width; with plain pointers a shared set
+  // made the compiler split them into 4-byte loads). The other modes choose
+  // rows per lane and keep a set per role.
+  static_assert(NW == 8, "the staging roles assume 8 waves");
+  constexpr bool kBuf = MODE == MODE_RETRIEVAL;
   const int st_t = tid & 255;
-  const bool stage_k = !kSplitStage || wave >= 4;
-  const bool stage_v = !kSplitStage || wave < 4;
+  const bool stage_k = wave >= 4;
   const int kr_row = st_t >> 2, kr_d0 = (st_t & 3) * (D / 4);
   const int vg = st_t & 15, vdc = st_t >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
-  const bool v_active = stage_v && vdc < D / 8;
-  u32x4 kreg[KLD], vreg[4];
-  auto load_tile = [&](int p0) {
-    if (stage_k) {
+  const bool v_active = !stage_k && vdc < D / 8;
+  u32x4 kreg[4];                    // K: KLD chunks of a row (and V in retrieval mode)
+  u32x4 vown[kBuf ? 1 : 4];        // V: one d-chunk of 4 keys
+  auto vreg = [&](int r) -> u32x4& {
+    if constexpr (kBuf) return kreg[r];
+    else return vown[r];
+  };
+  const int64_t hoff = ((int64_t)b * a.Hr + kv) * a.cap * D;
+  const uint32_t rbytes = kBuf ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t krs = wave_rsrc(a.kc + (kBuf ? hoff : 0), rbytes);
+  const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(a.vc + (kBuf ? hoff : 0), rbytes);
+  const uint32_t k_voff = (uint32_t)(kr_row * D + kr_d0) * 2u;
+  const uint32_t v_voff = (uint32_t)(4 * vg * D + 8 * vdc) * 2u;
+  auto load_k = [&](int p0) {
+    if constexpr (kBuf) {
+      const uint32_t o = k_voff + (uint32_t)p0 * (uint32_t)(D * 2);
+#pragma unroll
+      for (int c = 0; c < KLD; ++c) kreg[c] = buf_ld16(krs, o + 16 * c, 0);
+    } else {
       const uint16_t* kp = KeySrc<D>::template row<MODE>(a, b, kv, p0 + kr_row, false) + kr_d0;
 #pragma unroll
       for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
     }
-    if (v_active) {
+  };
+  auto load_v = [&](int p0) {
+    if constexpr (kBuf) {
+      const uint32_t o = v_voff + (uint32_t)p0 * (uint32_t)(D * 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vreg(r) = buf_ld16(vrs, o + (uint32_t)(r * D * 2), 0);
+    } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[r] = ld16(KeySrc<D>::template row<MODE>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+        vreg(r) = ld16(KeySrc<D>::template row<MODE>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_k = [&](int stage) {
     uint16_t* ks = Ks[stage];
+#pragma unroll
+    for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+  };
+  auto store_v = [&](int stage) {
     uint16_t* vt = Vt[stage];
-    if (stage_k) {
 #pragma unroll
-      for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
+    for (int i = 0; i < 8; ++i) {
+      const int d = 8 * vdc + i;
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t lo = __builtin_amdgcn_perm(word_of(vreg(1), i >> 1), word_of(vreg(0), i >> 1), sel);
+      uint32_t hi = __builtin_amdgcn_perm(word_of(vreg(3), i >> 1), word_of(vreg(2), i >> 1), sel);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vt + d * kBN + 4 * vt_slot(vg, d));
+      dst[0] = lo;
+      dst[1] = hi;
     }
-    if (v_active) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = 8 * vdc + i;
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t lo = __builtin_amdgcn_perm(word_of(vreg[1], i >> 1), word_of(vreg[0], i >> 1), sel);
-        uint32_t hi = __builtin_amdgcn_perm(word_of(vreg[3], i >> 1), word_of(vreg[2], i >> 1), sel);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vt + d * kBN + 4 * vt_slot(vg, d));
-        dst[0] = lo;
-        dst[1] = hi;
-      }
-    }
+  };
+  auto load_tile = [&](int p0) {
+    if (stage_k) load_k(p0);
+    if (v_active) load_v(p0);
+  };
+  auto store_tile = [&](int stage) {
+    if (stage_k) store_k(stage);
+    if (v_active) store_v(stage);
   };
 
   // ---- state --------------------------------------------------------------------
@@ -269,7 +306,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // B operands of the four 16-key slices.
   const float c2 = a.scale_log2;
   const float lazy = 8.0f / c2;  // raw-score growth that forces a rescale
-  auto softmax_update = [&](const float (&sc)[2][16], float& m, float& l, f32x16 (&O)[DB],
+  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB],
                             bf16x8 (&pb)[4]) {
     float tm = -INFINITY;
 #pragma unroll
@@ -336,66 +373,41 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     }
   };
 
-  // ---- main loop ----------------------------------------------------------------
-  load_tile(tile_pos(0));
-  store_tile(0);
-  __syncthreads();
-  // Every load issued so far (the query fragments, tile 0) has landed: say so
-  // explicitly. Without it the wait-count insertion merges the path on which
-  // no tile store waited into the loop header and keeps the query loads
-  // "pending", so each iteration's QK products would wait for the next tile's
-  // prefetch (vmcnt counts in order), exposing its whole latency.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  for (int k = 0; k < ntiles; ++k) {
+  // S^T = K Q^T for the 64 keys of the K tile at ks (two 32-key blocks). All
+  // K fragments of a block are requested before its first product (as for V
+  // above), and the two blocks' independent accumulation chains are
+  // interleaved.
+  auto qk = [&](const uint16_t* ks, f32x16 (&st)[2]) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+    const uint16_t* krow0 = ks + q32 * KPAD + 8 * h2;
+    const uint16_t* krow1 = krow0 + 32 * KPAD;
+    bf16x8 ak0[KS], ak1[KS];
+#pragma unroll
+    for (int ks_ = 0; ks_ < KS; ++ks_)
+      ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks_));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks_ = 0; ks_ < KS; ++ks_)
+      ak1[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks_));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks_ = 0; ks_ < KS; ++ks_) {
+      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks_], qf[ks_], st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks_], qf[ks_], st[1], 0, 0, 0);
+    }
+  };
+  // Masked scores, softmax update and PV product of tile k from its raw
+  // scores st and V tile vt. Tiles wholly below the wave's first query need
+  // no causal mask, tiles wholly above its last query are skipped.
+  auto consume = [&](int k, f32x16 (&st)[2], const uint16_t* vt) {
     const int p0 = tile_pos(k);
-    const int stage = k & 1;
-    const bool more = k + 1 < ntiles;
-    if (more) load_tile(tile_pos(k + 1));
-    if (kMixed && k == nlam) {
-      // end of the Lambda phase: keep (1 - alpha) * O / l, restart the state
-      const float ll = l_f + __shfl_xor(l_f, 32, 64);
-      const float wl = (1.0f - alpha) / ll;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
-        o_f[db] = f32x16{};
-      }
-      m_f = -INFINITY;
-      l_f = 0.0f;
-    }
     const bool lam_phase = MODE == MODE_STREAMING || (kMixed && k < nlam);
-
-    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks). All K
-    // fragments of a block are requested before its first product (as for V
-    // above), and the two blocks' independent accumulation chains are
-    // interleaved.
-    f32x16 st[2] = {f32x16{}, f32x16{}};
-    {
-      const uint16_t* krow0 = Ks[stage] + q32 * KPAD + 8 * h2;
-      const uint16_t* krow1 = krow0 + 32 * KPAD;
-      bf16x8 ak0[KS], ak1[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ak0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks));
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ak1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks));
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks], qf[ks], st[0], 0, 0, 0);
-        st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks], qf[ks], st[1], 0, 0, 0);
-      }
-    }
-    // raw scores with this mode's mask; tiles wholly below the wave's first
-    // query need no causal mask, tiles wholly above its last query are skipped
     const bool live = p0 <= i_wlast;
     const bool diag = p0 + kBN - 1 > i_wfirst;
     if (live) {
-      float sf[2][16];
+      // masked in place: unmasked tiles use the product registers as they are
+      // (a separate masked copy cost 32 moves per tile on the unmasked path)
       if (lam_phase || diag) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -405,21 +417,52 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
             // bitwise operators: a select per element, no per-lane branches
             const bool causal = jp <= i_q;
             const bool lam = causal & ((jp < a.S) | (i_q - jp < a.R));
-            sf[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
+            st[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
           }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sf[kb][j] = st[kb][j];
       }
       bf16x8 pb[4];
-      softmax_update(sf, m_f, l_f, o_f, pb);
-      pv(Vt[stage], pb, o_f);
+      softmax_update(st, m_f, l_f, o_f, pb);
+      pv(vt, pb, o_f);
     }
-    // the other stage was last read before the previous barrier
-    if (more) store_tile(stage ^ 1);
+  };
+
+  // ---- main loop ----------------------------------------------------------------
+  {
+    load_tile(tile_pos(0));
+    store_tile(0);
     __syncthreads();
+    // Every load issued so far (the query fragments, tile 0) has landed: say
+    // so explicitly. Without it the wait-count insertion merges the path on
+    // which no tile store waited into the loop header and keeps the query
+    // loads "pending", so each iteration's QK products would wait for the
+    // next tile's prefetch (vmcnt counts in order), exposing its whole
+    // latency.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int k = 0; k < ntiles; ++k) {
+      const int stage = k & 1;
+      const bool more = k + 1 < ntiles;
+      if (more) load_tile(tile_pos(k + 1));
+      if (kMixed && k == nlam) {
+        // end of the Lambda phase: keep (1 - alpha) * O / l, restart the state
+        const float ll = l_f + __shfl_xor(l_f, 32, 64);
+        const float wl = (1.0f - alpha) / ll;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
+          o_f[db] = f32x16{};
+        }
+        m_f = -INFINITY;
+        l_f = 0.0f;
+      }
+      f32x16 st[2];
+      qk(Ks[stage], st);
+      consume(k, st, Vt[stage]);
+      // the other stage was last read before the previous barrier
+      if (more) store_tile(stage ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------------
