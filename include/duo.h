@@ -161,7 +161,8 @@ duo_status duo_decode(duo_layer* layer, const void* q, const void* k_new, const 
  * out_h = alpha[h/G] * full_h + (1 - alpha[h/G]) * streaming_h over one
  * sequence of `seq_len` tokens. q [B, T, Hq, D] bf16, k/v [B, T, Hkv, D]
  * (kv_dtype must be BF16), alpha [Hkv] fp32 on the device; the descriptor's
- * retrieval fields are ignored. */
+ * retrieval fields are ignored. A sequence whose K (or V) tensor holds
+ * 2^31 bytes or more (seq_len * Hkv * D * 2) returns DUO_ERR_UNSUPPORTED. */
 duo_status duo_mixed_forward(const duo_layer_desc* desc, const void* q, const void* k,
                              const void* v, const float* alpha, int32_t seq_len, void* out,
                              hipStream_t stream);

@@ -265,6 +265,9 @@ duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void*
     return st;
   if (!alpha) return DUO_ERR_INVALID_ARG;
   if (!aligned(alpha, 4)) return DUO_ERR_LAYOUT;
+  // the kernel reads one KV head's rows of a sequence through a 32-bit range
+  if ((int64_t)T * d->n_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
+    return DUO_ERR_UNSUPPORTED;
   if (launch_mixed(*d, q, k, v, alpha, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
   return DUO_OK;
 }

@@ -87,48 +87,33 @@ __device__ __forceinline__ int vt_slot(int c, int d) {
   return (((pair ^ ((d >> 1) & 7)) << 1) | half);
 }
 
+// Row lookup of streaming mode: base of key row `p` (absolute position).
+// Three sources: the chunk itself, the ring (sink slots, then the recent
+// window), and a fixed chunk row for positions no query of the launch may
+// attend (the mask removes them), so every address stays inside its buffer.
+// All three are computed and one is selected, with no per-lane branch. A
+// window position p (n - R <= p < n) has ring slot S + (p - S) mod R =
+// S + (c0 + R + p - n) mod R with the uniform c0 = (n - S) mod R, and
+// c0 + R + p - n lies in [c0, c0 + R): one conditional subtract instead of a
+// per-lane division.
 template <int D>
-struct KeySrc {
-  // Base of key row `p` (absolute position) for the given mode. Positions no
-  // query of the launch may attend are mapped to some valid row (the mask
-  // removes them), so every address stays inside its buffer.
-  template <int MODE>
-  static __device__ __forceinline__ const uint16_t* row(const AttnArgs& a, int b, int kv, int p,
+__device__ __forceinline__ const uint16_t* stream_row(const AttnArgs& a, int b, int kv, int p,
                                                       bool v) {
-    if constexpr (MODE == MODE_RETRIEVAL) {
-      const int nk = a.n + a.T;
-      const int pc = p < nk ? (p < 0 ? 0 : p) : nk - 1;
-      const uint16_t* base = v ? a.vc : a.kc;
-      return base + (((int64_t)b * a.Hr + kv) * a.cap + pc) * D;
-    } else if constexpr (MODE == MODE_MIXED) {
-      const int pc = p < a.T ? (p < 0 ? 0 : p) : a.T - 1;
-      const uint16_t* base = v ? a.v_in : a.k_in;
-      return base + (((int64_t)b * a.T + pc) * a.Hkv + kv) * D;
-    } else {
-      // Three sources: the chunk itself, the ring (sink slots, then the
-      // recent window), and a fixed chunk row for positions no query of the
-      // launch may attend. All three are computed and one is selected, with
-      // no per-lane branch. A window position p (n - R <= p < n) has ring
-      // slot S + (p - S) mod R = S + (c0 + R + p - n) mod R with the uniform
-      // c0 = (n - S) mod R, and c0 + R + p - n lies in [c0, c0 + R): one
-      // conditional subtract instead of a per-lane division.
-      const bool chunk = p >= a.n && p < a.n + a.T;
-      const int rlo = a.n - a.R > a.S ? a.n - a.R : a.S;
-      const bool ring = !chunk && p >= 0 && p < a.n && (p < a.S || p >= rlo);
-      const int c0 = (int)((uint32_t)(a.n > a.S ? a.n - a.S : 0) % (uint32_t)a.R);
-      const int q = c0 + a.R + (p - a.n);
-      const int slot = p < a.S ? p : a.S + (q >= a.R ? q - a.R : q);
-      const int64_t i_chunk = ((int64_t)b * a.T + (p - a.n)) * a.Hkv + kv;
-      const int64_t i_ring = ((int64_t)b * a.Hs + (kv - a.Hr)) * (a.S + a.R) + slot;
-      const int64_t i_mask = (int64_t)b * a.T * a.Hkv + kv;
-      // both bases in scalar registers, so the per-lane choice is a register
-      // select (not a load of the chosen pointer from the argument block)
-      const uint16_t* ring_base = wave_ptr(v ? a.vr : a.kr);
-      const uint16_t* in_base = wave_ptr(v ? a.v_in : a.k_in);
-      return (ring ? ring_base : in_base) + (chunk ? i_chunk : ring ? i_ring : i_mask) * D;
-    }
-  }
-};
+  const bool chunk = p >= a.n && p < a.n + a.T;
+  const int rlo = a.n - a.R > a.S ? a.n - a.R : a.S;
+  const bool ring = !chunk && p >= 0 && p < a.n && (p < a.S || p >= rlo);
+  const int c0 = (int)((uint32_t)(a.n > a.S ? a.n - a.S : 0) % (uint32_t)a.R);
+  const int q = c0 + a.R + (p - a.n);
+  const int slot = p < a.S ? p : a.S + (q >= a.R ? q - a.R : q);
+  const int64_t i_chunk = ((int64_t)b * a.T + (p - a.n)) * a.Hkv + kv;
+  const int64_t i_ring = ((int64_t)b * a.Hs + (kv - a.Hr)) * (a.S + a.R) + slot;
+  const int64_t i_mask = (int64_t)b * a.T * a.Hkv + kv;
+  // both bases in scalar registers, so the per-lane choice is a register
+  // select (not a load of the chosen pointer from the argument block)
+  const uint16_t* ring_base = wave_ptr(v ? a.vr : a.kr);
+  const uint16_t* in_base = wave_ptr(v ? a.v_in : a.k_in);
+  return (ring ? ring_base : in_base) + (chunk ? i_chunk : ring ? i_ring : i_mask) * D;
+}
 
 // Waves per block: 8 (each staged K/V tile serves 256 query rows; waves 0-3
 // stage V, waves 4-7 stage K).
@@ -204,52 +189,62 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 
   // ---- global -> register staging of one K/V tile ------------------------------
   // 256 threads stage K and 256 stage V; the roles are wave-uniform.
-  // Retrieval mode reads the head's cached rows as one buffer resource (rows
-  // at or past the chunk's end read as zeros; the causal mask removes them),
-  // so a tile's addresses are one add per lane (53 fewer VALU per tile than
-  // per-row pointers), and both roles load into one set of registers (the
-  // 128-bit buffer loads keep their width; with plain pointers a shared set
-  // made the compiler split them into 4-byte loads). The other modes choose
-  // rows per lane and keep a set per role.
+  // Retrieval mode (the head's cached rows) and the mixed forward (the
+  // sequence's rows of one KV head, a row stride of Hkv*D) read K and V each
+  // as one buffer resource. Rows at or past the last key read as zeros (the
+  // causal mask removes them), a tile's addresses are one add per lane (53
+  // fewer VALU per tile than per-row pointers), and both roles load into one
+  // set of registers (the 128-bit buffer loads keep their width; with plain
+  // pointers a shared set made the compiler split them into 4-byte loads).
+  // Streaming mode gathers rows per lane from the ring and the chunk and
+  // keeps a set per role.
   static_assert(NW == 8, "the staging roles assume 8 waves");
-  constexpr bool kBuf = MODE == MODE_RETRIEVAL;
+  constexpr bool kBuf = MODE != MODE_STREAMING;
   const int st_t = tid & 255;
   const bool stage_k = wave >= 4;
   const int kr_row = st_t >> 2, kr_d0 = (st_t & 3) * (D / 4);
   const int vg = st_t & 15, vdc = st_t >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
   const bool v_active = !stage_k && vdc < D / 8;
-  u32x4 kreg[4];                    // K: KLD chunks of a row (and V in retrieval mode)
-  u32x4 vown[kBuf ? 1 : 4];        // V: one d-chunk of 4 keys
+  u32x4 kreg[4];                    // K: KLD chunks of a row (and V when kBuf)
+  u32x4 vown[kBuf ? 1 : 4];         // V: one d-chunk of 4 keys
   auto vreg = [&](int r) -> u32x4& {
     if constexpr (kBuf) return kreg[r];
     else return vown[r];
   };
-  const int64_t hoff = ((int64_t)b * a.Hr + kv) * a.cap * D;
-  const uint32_t rbytes = kBuf ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2) : 0u;
-  const __amdgpu_buffer_rsrc_t krs = wave_rsrc(a.kc + (kBuf ? hoff : 0), rbytes);
-  const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(a.vc + (kBuf ? hoff : 0), rbytes);
-  const uint32_t k_voff = (uint32_t)(kr_row * D + kr_d0) * 2u;
-  const uint32_t v_voff = (uint32_t)(4 * vg * D + 8 * vdc) * 2u;
+  // buffer view: row stride, first element and readable bytes (the host
+  // keeps every such range below 2^31 bytes)
+  const uint32_t rstride = (uint32_t)(MODE == MODE_RETRIEVAL ? D * 2 : a.Hkv * D * 2);
+  const int64_t hoff = MODE == MODE_RETRIEVAL ? ((int64_t)b * a.Hr + kv) * a.cap * D
+                                              : ((int64_t)b * a.T * a.Hkv + kv) * D;
+  const uint32_t rbytes =
+      MODE == MODE_RETRIEVAL ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2)
+                             : (uint32_t)((int64_t)a.T * a.Hkv - kv) * (uint32_t)(D * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      wave_rsrc((MODE == MODE_RETRIEVAL ? a.kc : a.k_in) + (kBuf ? hoff : 0), kBuf ? rbytes : 0u);
+  const __amdgpu_buffer_rsrc_t vrs =
+      wave_rsrc((MODE == MODE_RETRIEVAL ? a.vc : a.v_in) + (kBuf ? hoff : 0), kBuf ? rbytes : 0u);
+  const uint32_t k_voff = (uint32_t)kr_row * rstride + (uint32_t)kr_d0 * 2u;
+  const uint32_t v_voff = (uint32_t)(4 * vg) * rstride + (uint32_t)(8 * vdc) * 2u;
   auto load_k = [&](int p0) {
     if constexpr (kBuf) {
-      const uint32_t o = k_voff + (uint32_t)p0 * (uint32_t)(D * 2);
+      const uint32_t o = k_voff + (uint32_t)p0 * rstride;
 #pragma unroll
       for (int c = 0; c < KLD; ++c) kreg[c] = buf_ld16(krs, o + 16 * c, 0);
     } else {
-      const uint16_t* kp = KeySrc<D>::template row<MODE>(a, b, kv, p0 + kr_row, false) + kr_d0;
+      const uint16_t* kp = stream_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
 #pragma unroll
       for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
     }
   };
   auto load_v = [&](int p0) {
     if constexpr (kBuf) {
-      const uint32_t o = v_voff + (uint32_t)p0 * (uint32_t)(D * 2);
+      const uint32_t o = v_voff + (uint32_t)p0 * rstride;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vreg(r) = buf_ld16(vrs, o + (uint32_t)(r * D * 2), 0);
+      for (int r = 0; r < 4; ++r) vreg(r) = buf_ld16(vrs, o + (uint32_t)r * rstride, 0);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg(r) = ld16(KeySrc<D>::template row<MODE>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+        vreg(r) = ld16(stream_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
     }
   };
   auto store_k = [&](int stage) {

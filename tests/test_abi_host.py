@@ -135,6 +135,9 @@ def test_mixed_forward_validation():
     assert f(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 16, 0x1000, None) == 1
     d16 = _desc(kv_dtype="fp16")
     assert f(ctypes.byref(d16), 0x1000, 0x1000, 0x1000, 0x1000, 16, 0x1000, None) == 2
+    # a K tensor of 2^31 bytes (T * Hkv * D * 2) is beyond the kernel's 32-bit range
+    big = (1 << 31) // (8 * 128 * 2)
+    assert f(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, big, 0x1000, None) == 2
 
 
 def test_status_strings():
