@@ -27,6 +27,7 @@ from .attention import (allowed_mask, masked_attention, layer_attention,
 from .cache import ring_slot, ring_positions_after, OracleLayer
 from .int4 import quantize_int4_g32, dequantize_int4_g32, pack_nibbles, unpack_nibbles
 from .routing import head_permutation, apply_head_permutation, invert_permutation
+from .gates import mixed_alpha_grad, binarize_gates, reorder_head_rows
 
 __all__ = [
     "allowed_mask", "masked_attention", "layer_attention", "mixed_attention",
@@ -34,4 +35,5 @@ __all__ = [
     "ring_slot", "ring_positions_after", "OracleLayer",
     "quantize_int4_g32", "dequantize_int4_g32", "pack_nibbles", "unpack_nibbles",
     "head_permutation", "apply_head_permutation", "invert_permutation",
+    "mixed_alpha_grad", "binarize_gates", "reorder_head_rows",
 ]
