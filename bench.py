@@ -17,8 +17,9 @@ HBM before any timed region.
 The same line carries the other workloads under "workloads": the 8-head D=64
 layer (prefill 1024 + 16 decode steps, latency), the Llama-3-8B GQA chunked
 prefill (65536 tokens in 8192-token chunks, TFLOP/s), the alpha-blend mixed
-forward (Llama-2-7B shape, 16384 tokens, TFLOP/s) and the Llama-3-8B 4-bit
-decode at a 1,048,576-token context (KV GB/s, tok/s).
+forward (Llama-2-7B shape, 16384 tokens, TFLOP/s), its gradient with respect
+to the gates at the same size (TFLOP/s over the same attention pairs) and the
+Llama-3-8B 4-bit decode at a 1,048,576-token context (KV GB/s, tok/s).
 
 `--gpus N` with N > 1 is refused: this build measures one GPU.
 """
@@ -340,6 +341,33 @@ def bench_mixed(args, dev):
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def bench_mixed_alpha_grad(args, dev):
+    """Gradient with respect to the gates at the identification size: the
+    same two attentions as the gate-blended forward (recomputed; no stored
+    activations), dotted with dout, plus the per-head reduction."""
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import WORKLOADS, device_normal
+    w = WORKLOADS["llama2_7b_mixed_16k"]
+    H, D, T = w.n_q_heads, w.head_dim, w.mixed_tokens
+    q = device_normal((1, T, H, D), 41, dev, torch.bfloat16)
+    k = device_normal((1, T, H, D), 42, dev, torch.bfloat16)
+    v = device_normal((1, T, H, D), 43, dev, torch.bfloat16)
+    dout = device_normal((1, T, H, D), 45, dev, torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(44)
+    alpha = torch.rand((H,), generator=g, device=dev, dtype=torch.float32)
+    grad = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)  # 8 KiB needed
+    fn = lambda: duo.mixed_alpha_grad(q, k, v, dout, alpha, softmax_scale=w.softmax_scale,  # noqa: E731
+                                      l1_weight=0.05, grad=grad, workspace=ws)
+    fn()
+    ms = sorted(time_region(torch, fn) for _ in range(5))[2]
+    flops = H * (causal_pairs(0, T) + lambda_pairs(0, T, w.sink, w.recent)) * 4 * D
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tflop": flops / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def bench_int4_decode(args, dev):
     import torch
     import kv_cache_compression_duo_amd as duo
@@ -422,7 +450,7 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of: decode,mha8,prefill,mixed,int4")
+    ap.add_argument("--only", default="", help="comma list of: decode,mha8,prefill,mixed,grad,int4")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the counter runs measure")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -462,6 +490,7 @@ def main():
     for name, key, fn in (("mha8", "mha8_d64_seq1024", bench_mha8),
                           ("prefill", "llama3_8b_prefill_64k", bench_prefill_llama3),
                           ("mixed", "llama2_7b_mixed_16k", bench_mixed),
+                          ("grad", "llama2_7b_mixed_alpha_grad_16k", bench_mixed_alpha_grad),
                           ("int4", "llama3_8b_int4_decode_1m", bench_int4_decode)):
         if want(name):
             work[key] = fn(args, dev)

@@ -167,6 +167,33 @@ duo_status duo_mixed_forward(const duo_layer_desc* desc, const void* q, const vo
                              const void* v, const float* alpha, int32_t seq_len, void* out,
                              hipStream_t stream);
 
+/* Workspace (device memory, 16-byte aligned) that duo_mixed_alpha_grad needs
+ * for seq_len tokens: one fp32 partial sum per attention block. Returns 0 for
+ * an invalid descriptor or seq_len < 1. */
+size_t duo_mixed_alpha_grad_workspace(const duo_layer_desc* desc, int32_t seq_len);
+
+/* Gradient of the head-identification loss with respect to the gates of the
+ * gate-blended forward (xllm-io review "DuoAttention: Efficient Long-Context
+ * LLM Inference with Retrieval and Streaming Heads", section 三 核心公式:
+ * the gate-blended attention, the distillation loss and the L1 term over the
+ * gates; 检索头识别: only the gates are trained). With dout [B, T, Hq, D] bf16
+ * the gradient of the distillation loss with respect to the gate-blended
+ * output, writes
+ *   grad_alpha[kv] = sum over the batch, the tokens, the query heads of KV head
+ *                    kv and the channels of dout * (full - streaming)
+ *                    + l1_weight * sign(alpha[kv])   (sign(0) taken as 0).
+ * q/k/v and the size limit as for duo_mixed_forward; alpha and grad_alpha
+ * [Hkv] fp32 on the device (alpha enters only through the L1 term). The
+ * workspace (device, at least duo_mixed_alpha_grad_workspace bytes) is
+ * overwritten; the sum over it runs in a fixed order, so the result is
+ * reproducible. A missing, misaligned or short workspace returns
+ * DUO_ERR_INVALID_ARG / DUO_ERR_LAYOUT; other errors as for
+ * duo_mixed_forward. */
+duo_status duo_mixed_alpha_grad(const duo_layer_desc* desc, const void* q, const void* k,
+                                const void* v, const void* dout, const float* alpha,
+                                float l1_weight, int32_t seq_len, float* grad_alpha,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Host-only: stable permutation that makes retrieval heads contiguous.
  * mask[h] != 0 marks KV head h as a retrieval head. perm_out[i] receives the
  * original KV head placed at position i (retrieval heads ascending, then

@@ -184,6 +184,36 @@ def mixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     return out
 
 
+def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                     alpha: torch.Tensor, *, softmax_scale: float, sink: int = 16,
+                     recent: int = 64, l1_weight: float = 0.0, grad=None, workspace=None):
+    """Gradient with respect to the gates of mixed_forward:
+    grad[kv] = sum of dout * (full - streaming) over the batch, tokens, the
+    query heads of KV head kv and channels, + l1_weight * sign(alpha[kv]).
+    dout [B,T,Hq,D] bf16; returns grad [Hkv] fp32 (device). The workspace
+    (uint8 device tensor) is allocated here unless given."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16)
+    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16)
+    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16)
+    _check_act(dout, "dout", (B, T, Hq, D), torch.bfloat16)
+    _check_act(alpha, "alpha", (Hkv,), torch.float32)
+    if grad is None:
+        grad = torch.empty(Hkv, dtype=torch.float32, device=q.device)
+    _check_act(grad, "grad", (Hkv,), torch.float32)
+    desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
+                     sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
+    need = int(lib.duo_mixed_alpha_grad_workspace(byref(desc), T))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib.duo_mixed_alpha_grad(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                   _ptr(alpha), float(l1_weight), T, _ptr(grad),
+                                   _ptr(workspace), workspace.numel(), _stream_ptr(q.device)),
+          "duo_mixed_alpha_grad")
+    return grad
+
+
 def head_permutation(mask: Sequence[int]):
     """Stable permutation making retrieval KV heads contiguous (host call).
     Returns (perm, n_retrieval): perm[i] = original KV head at position i."""

@@ -272,6 +272,34 @@ duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void*
   return DUO_OK;
 }
 
+size_t duo_mixed_alpha_grad_workspace(const duo_layer_desc* d, int32_t T) {
+  if (check_desc(d) != DUO_OK || T < 1) return 0;
+  return align_up(mixed_grad_partials(*d, T) * sizeof(float), 256);
+}
+
+duo_status duo_mixed_alpha_grad(const duo_layer_desc* d, const void* q, const void* k,
+                                const void* v, const void* dout, const float* alpha,
+                                float l1_weight, int32_t T, float* grad, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  duo_status st = check_desc(d);
+  if (st != DUO_OK) return st;
+  if (d->kv_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (T < 1 || !isfinite(l1_weight)) return DUO_ERR_INVALID_ARG;
+  if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
+      (st = check_act(v)) != DUO_OK || (st = check_act(dout)) != DUO_OK)
+    return st;
+  if (!alpha || !grad || !ws) return DUO_ERR_INVALID_ARG;
+  if (!aligned(alpha, 4) || !aligned(grad, 4) || !aligned(ws, 16)) return DUO_ERR_LAYOUT;
+  if (ws_bytes < mixed_grad_partials(*d, T) * sizeof(float)) return DUO_ERR_INVALID_ARG;
+  // the kernel reads one KV head's rows of a sequence through a 32-bit range
+  if ((int64_t)T * d->n_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
+    return DUO_ERR_UNSUPPORTED;
+  if (launch_mixed_alpha_grad(*d, q, k, v, dout, alpha, l1_weight, T, grad,
+                              static_cast<float*>(ws), stream) != hipSuccess)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
 duo_status duo_head_permutation(const uint8_t* mask, int32_t n, int32_t* perm,
                                 int32_t* n_retrieval) {
   if (!mask || !perm || !n_retrieval || n < 1) return DUO_ERR_INVALID_ARG;

@@ -45,7 +45,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum { MODE_RETRIEVAL = 0, MODE_STREAMING = 1, MODE_MIXED = 2 };
+enum { MODE_RETRIEVAL = 0, MODE_STREAMING = 1, MODE_MIXED = 2, MODE_GRAD = 3 };
 
 struct AttnArgs {
   const uint16_t* q;     // [B][T][Hq][D]
@@ -57,6 +57,8 @@ struct AttnArgs {
   const uint16_t* kr;    // ring [B][Hs][S+R][D]
   const uint16_t* vr;
   const float* alpha;    // [Hkv] (mixed)
+  const uint16_t* dout;  // [B][T][Hq][D] bf16 (gate gradient)
+  float* partial;        // [B][head groups][query tiles] (gate gradient)
   int T, Hq, Hkv, Hr, Hs, G, S, R;
   int64_t cap;
   int n;         // absolute position of token 0 of the chunk (0 for mixed)
@@ -130,6 +132,10 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   constexpr int KPAD = D + 8;         // K tile row stride in LDS (elements)
   constexpr int KLD = D / 32;         // 16-byte K loads per thread
   constexpr bool kMixed = MODE == MODE_MIXED;
+  constexpr bool kGrad = MODE == MODE_GRAD;
+  // the gate-blended forward and its gate gradient visit the Lambda tiles,
+  // then all causal tiles
+  constexpr bool kTwoPhase = kMixed || kGrad;
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
   // written to the other, so one barrier per tile suffices
   __shared__ __align__(16) uint16_t Ks[2][kBN * KPAD];
@@ -291,6 +297,24 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     return lam_lds[((wave * DB + db) * 8 + i) * 64 + lane];
   };
   const float alpha = kMixed ? a.alpha[kv] : 1.0f;
+  // Gate gradient: dout . (O / l) over this lane's channels of its query,
+  // the element (db, 4 jb + r) of O being channel 32 db + 8 jb + 4 h2 + r.
+  float g_lam = 0.0f;
+  auto dout_dot = [&](float inv_l) -> float {
+    const uint16_t* dp = a.dout + (((int64_t)b * a.T + t_qc) * a.Hq + head) * D + 4 * h2;
+    float acc = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint2 w = *reinterpret_cast<const uint2*>(dp + 32 * db + 8 * jb);
+        acc = fmaf(__uint_as_float(w.x << 16), o_f[db][4 * jb + 0], acc);
+        acc = fmaf(__uint_as_float(w.x & 0xffff0000u), o_f[db][4 * jb + 1], acc);
+        acc = fmaf(__uint_as_float(w.y << 16), o_f[db][4 * jb + 2], acc);
+        acc = fmaf(__uint_as_float(w.y & 0xffff0000u), o_f[db][4 * jb + 3], acc);
+      }
+    return acc * inv_l;
+  };
 
   // One online-softmax update of (m, l, O) from masked raw scores (m in raw
   // score units; the scale, folded with log2(e), enters the exp2 argument as
@@ -397,7 +421,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // no causal mask, tiles wholly above its last query are skipped.
   auto consume = [&](int k, f32x16 (&st)[2], const uint16_t* vt) {
     const int p0 = tile_pos(k);
-    const bool lam_phase = MODE == MODE_STREAMING || (kMixed && k < nlam);
+    const bool lam_phase = MODE == MODE_STREAMING || (kTwoPhase && k < nlam);
     const bool live = p0 <= i_wlast;
     const bool diag = p0 + kBN - 1 > i_wfirst;
     if (live) {
@@ -437,17 +461,22 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       const int stage = k & 1;
       const bool more = k + 1 < ntiles;
       if (more) load_tile(tile_pos(k + 1));
-      if (kMixed && k == nlam) {
-        // end of the Lambda phase: keep (1 - alpha) * O / l, restart the state
+      if (kTwoPhase && k == nlam) {
+        // end of the Lambda phase: keep (1 - alpha) * O / l (forward) or
+        // dout . O / l (gate gradient), restart the state
         const float ll = l_f + __shfl_xor(l_f, 32, 64);
-        const float wl = (1.0f - alpha) / ll;
+        if constexpr (kGrad) {
+          g_lam = dout_dot(1.0f / ll);
+        } else {
+          const float wl = (1.0f - alpha) / ll;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
-          o_f[db] = f32x16{};
+            for (int i = 0; i < 8; ++i)
+              lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
         m_f = -INFINITY;
         l_f = 0.0f;
       }
@@ -461,6 +490,25 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   }
 
   // ---- epilogue -----------------------------------------------------------------
+  if constexpr (kGrad) {
+    // dout . (full - streaming) summed over the block's rows and channels
+    // (all waves belong to one KV head); one partial per block, summed per
+    // KV head by the reduction kernel in a fixed order
+    const float lf = l_f + __shfl_xor(l_f, 32, 64);
+    float g = t_q < a.T ? dout_dot(1.0f / lf) - g_lam : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) g += __shfl_xor(g, off, 64);
+    __shared__ float gsum[NW];
+    if (lane == 0) gsum[wave] = g;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += gsum[w];
+      a.partial[((int64_t)b * a.Hkv * groups + hg) * a.n_qtiles + tq] = sum;
+    }
+    return;
+  }
   if (t_q >= a.T) return;
   const float lf = l_f + __shfl_xor(l_f, 32, 64);
   const float wf = alpha / lf;  // alpha = 1 outside the mixed forward
@@ -578,6 +626,71 @@ hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, c
   a.kv_base = 0;
   a.scale_log2 = d.softmax_scale * kLog2e;
   return launch_mode<MODE_MIXED>(a, d.head_dim, d.n_kv_heads, d.batch, s);
+}
+
+// Gate gradient: the flash pass writes one partial sum per block; this
+// kernel adds a KV head's partials in a fixed order (one block per KV head)
+// and the L1 term's gradient l1 * sign(alpha), taken as 0 at alpha = 0.
+__global__ __launch_bounds__(256) void alpha_grad_reduce_kernel(const float* __restrict__ partial,
+                                                                int B, int Hkv, int per_kv,
+                                                                const float* __restrict__ alpha,
+                                                                float l1, float* __restrict__ grad) {
+  __shared__ float red[256];
+  const int kv = blockIdx.x;
+  float s = 0.0f;
+  const int n = B * per_kv;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int bb = i / per_kv, j = i - bb * per_kv;
+    s += partial[((int64_t)bb * Hkv + kv) * per_kv + j];
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float al = alpha[kv];
+    grad[kv] = red[0] + l1 * (al > 0.0f ? 1.0f : (al < 0.0f ? -1.0f : 0.0f));
+  }
+}
+
+// Heads per block of the flash kernels for group size G (as launch_d picks).
+static int heads_per_block(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
+
+size_t mixed_grad_partials(const duo_layer_desc& d, int T) {
+  const int G = d.n_q_heads / d.n_kv_heads, HB = heads_per_block(G);
+  const int BMT = 32 * 8 / HB;
+  return (size_t)d.batch * d.n_kv_heads * (G / HB) * (size_t)((T + BMT - 1) / BMT);
+}
+
+hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const void* k,
+                                   const void* v, const void* dout, const float* alpha,
+                                   float l1_weight, int T, float* grad, float* partial,
+                                   hipStream_t s) {
+  AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_in = static_cast<const uint16_t*>(k);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.partial = partial;
+  a.alpha = alpha;
+  a.T = T;
+  a.Hq = d.n_q_heads;
+  a.Hkv = d.n_kv_heads;
+  a.G = d.n_q_heads / d.n_kv_heads;
+  a.S = d.sink;
+  a.R = d.recent;
+  a.n = 0;
+  a.kv_base = 0;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  hipError_t e = launch_mode<MODE_GRAD>(a, d.head_dim, d.n_kv_heads, d.batch, s);
+  if (e != hipSuccess) return e;
+  const int HB = heads_per_block(a.G), BMT = 32 * 8 / HB;
+  const int per_kv = (a.G / HB) * ((T + BMT - 1) / BMT);
+  alpha_grad_reduce_kernel<<<d.n_kv_heads, 256, 0, s>>>(partial, d.batch, d.n_kv_heads, per_kv,
+                                                        alpha, l1_weight, grad);
+  return hipGetLastError();
 }
 
 }  // namespace duo

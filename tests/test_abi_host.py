@@ -140,6 +140,37 @@ def test_mixed_forward_validation():
     assert f(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, big, 0x1000, None) == 2
 
 
+def test_mixed_alpha_grad_workspace_and_validation():
+    L = _lib()
+    f, ws = L.lib.duo_mixed_alpha_grad, L.lib.duo_mixed_alpha_grad_workspace
+    d = _desc(n_q_heads=32, n_kv_heads=32, n_retrieval_kv_heads=0)
+    # G = 1: one query head per block of 8 x 32 = 256 tokens; one fp32 partial per block
+    assert ws(ctypes.byref(d), 16384) == 32 * 64 * 4
+    assert ws(ctypes.byref(d), 257) == 32 * 2 * 4 + 0  # 256 B granularity: 256 already
+    assert ws(ctypes.byref(d), 0) == 0
+    dg = _desc()  # 32 q / 8 kv: G = 4, four query heads per block of 64 tokens
+    assert ws(ctypes.byref(dg), 1000) == 256 * ((8 * 16 * 4 + 255) // 256)
+    P, need = 0x1000, ws(ctypes.byref(d), 100)
+    args = lambda **kw: [kw.get(n, dv) for n, dv in (  # noqa: E731
+        ("q", P), ("k", P), ("v", P), ("dout", P), ("alpha", P), ("l1", 0.05), ("T", 100),
+        ("grad", P), ("ws", P), ("ws_bytes", need))]
+    # every case below fails validation before any HIP call
+    assert f(ctypes.byref(d), *args(T=0), None) == 1
+    assert f(ctypes.byref(d), *args(ws=None), None) == 1
+    exact = 32 * 1 * 4  # T = 100: one 256-token tile per head (need rounds it up to 256 B)
+    assert need >= exact
+    assert f(ctypes.byref(d), *args(ws_bytes=exact - 4), None) == 1
+    assert f(ctypes.byref(d), *args(grad=None), None) == 1
+    assert f(ctypes.byref(d), *args(l1=float("inf")), None) == 1
+    assert f(ctypes.byref(d), *args(ws=0x1004), None) == 3
+    assert f(ctypes.byref(d), *args(dout=0x1008), None) == 3
+    assert f(ctypes.byref(d), *args(grad=0x1002), None) == 3
+    d16 = _desc(n_q_heads=32, n_kv_heads=32, n_retrieval_kv_heads=0, kv_dtype="fp16")
+    assert f(ctypes.byref(d16), *args(), None) == 2
+    big = (1 << 31) // (32 * 128 * 2)
+    assert f(ctypes.byref(d), *args(T=big, ws_bytes=1 << 40), None) == 2
+
+
 def test_status_strings():
     L = _lib()
     assert L.status_string(0) == "ok"
