@@ -202,6 +202,28 @@ duo_status duo_mixed_alpha_grad(const duo_layer_desc* desc, const void* q, const
 duo_status duo_head_permutation(const uint8_t* mask, int32_t n_kv_heads, int32_t* perm_out,
                                 int32_t* n_retrieval_out);
 
+/* Host-only: retrieval mask from trained gates (xllm-io review, section 三
+ * 检索头识别, step 3: alpha is binarized as 1[alpha >= tau]; paperlayer
+ * summary, section 2, Binarizing Attention Implementations: tau is the
+ * sparsity quantile of the gates). Of the n gates, k = floor(sparsity * n)
+ * (in double precision) become streaming heads: tau is the (k+1)-th smallest
+ * gate and mask_out[i] = (alpha[i] >= tau), so gates tied with tau stay
+ * retrieval heads; k = n marks every head streaming. sparsity must lie in
+ * [0, 1]; a NaN gate, n < 1 or a null pointer returns DUO_ERR_INVALID_ARG.
+ * mask_out[n] (1 = retrieval) is the caller's. */
+duo_status duo_binarize_gates(const float* alpha, int32_t n, double sparsity, uint8_t* mask_out);
+
+/* Host-only: moves whole head blocks of a row-major matrix so that block i of
+ * `out` is block perm[i] of `in`, a block being rows_per_head rows of
+ * row_bytes bytes. Applied to the query/key/value projection weights (output
+ * rows) with the permutation of duo_head_permutation (a KV head's query heads
+ * moving together), it makes the retrieval heads contiguous, as the caches
+ * here expect (xllm-io review, section 三 模型部署优化). in and out are the
+ * caller's host buffers and must not overlap (DUO_ERR_LAYOUT); a perm that is
+ * not a permutation of [0, n_heads) returns DUO_ERR_INVALID_ARG. */
+duo_status duo_reorder_head_rows(const void* in, void* out, const int32_t* perm, int32_t n_heads,
+                                 int64_t rows_per_head, int64_t row_bytes);
+
 /* Host-only: ring slot of token position p (the rule stated above), or -1
  * for invalid arguments. */
 int32_t duo_ring_slot(int64_t position, int32_t sink, int32_t recent);

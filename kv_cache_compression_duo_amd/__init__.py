@@ -7,7 +7,9 @@ run in hand-written HIP kernels behind the C ABI of include/duo.h; this
 package is the thin ctypes binding (torch supplies device memory and streams).
 """
 from ._lib import DuoError, LIB_PATH, status_string
-from .api import DuoLayer, mixed_forward, mixed_alpha_grad, head_permutation, ring_slot
+from .api import (DuoLayer, mixed_forward, mixed_alpha_grad, binarize_gates, reorder_head_rows,
+                  head_permutation, ring_slot)
 
 __all__ = ["DuoError", "LIB_PATH", "status_string", "DuoLayer", "mixed_forward", "mixed_alpha_grad",
+           "binarize_gates", "reorder_head_rows",
            "head_permutation", "ring_slot"]

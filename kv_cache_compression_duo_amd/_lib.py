@@ -69,6 +69,10 @@ def _load():
                                          c_void_p, c_size_t, c_void_p]),
         "duo_head_permutation": (c_int, [POINTER(c_uint8), c_int32, POINTER(c_int32),
                                          POINTER(c_int32)]),
+        "duo_binarize_gates": (c_int, [POINTER(c_float), c_int32, ctypes.c_double,
+                                       POINTER(c_uint8)]),
+        "duo_reorder_head_rows": (c_int, [c_void_p, c_void_p, POINTER(c_int32), c_int32, c_int64,
+                                          c_int64]),
         "duo_ring_slot": (c_int32, [c_int64, c_int32, c_int32]),
         "duo_status_string": (c_char_p, [c_int]),
     }

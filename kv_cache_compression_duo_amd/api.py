@@ -9,7 +9,7 @@ forward. ``head_permutation`` and ``ring_slot`` are the host helpers.
 from __future__ import annotations
 
 import ctypes
-from ctypes import byref, c_int32, c_uint8, c_void_p
+from ctypes import POINTER, byref, c_float, c_int32, c_uint8, c_void_p
 from typing import Optional, Sequence
 
 import torch
@@ -212,6 +212,40 @@ def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: to
                                    _ptr(workspace), workspace.numel(), _stream_ptr(q.device)),
           "duo_mixed_alpha_grad")
     return grad
+
+
+def binarize_gates(alpha, sparsity: float):
+    """Retrieval mask (list of 0/1, 1 = retrieval) from trained gates (host
+    call): the floor(sparsity * n) smallest gates become streaming heads,
+    gates tied with the threshold stay retrieval heads."""
+    import numpy as np
+    if isinstance(alpha, torch.Tensor):
+        alpha = alpha.detach().to("cpu", torch.float32).numpy()
+    a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32).ravel())
+    n = int(a.size)
+    mask = (c_uint8 * max(n, 1))()
+    check(lib.duo_binarize_gates(a.ctypes.data_as(POINTER(c_float)), n, float(sparsity), mask),
+          "duo_binarize_gates")
+    return list(mask)[:n]
+
+
+def reorder_head_rows(w, perm: Sequence[int], rows_per_head: int):
+    """Host copy of a weight whose rows form head blocks of rows_per_head rows,
+    with block i of the result = block perm[i] of w (numpy array or CPU
+    tensor in, numpy array out)."""
+    import numpy as np
+    if isinstance(w, torch.Tensor):
+        w = w.detach().cpu().numpy()
+    src = np.ascontiguousarray(w)
+    n = len(perm)
+    if src.ndim < 1 or n < 1 or src.shape[0] != n * rows_per_head:
+        raise ValueError("weight rows must be n_heads * rows_per_head")
+    dst = np.empty_like(src)
+    row_bytes = src.nbytes // src.shape[0]
+    p = (c_int32 * n)(*[int(x) for x in perm])
+    check(lib.duo_reorder_head_rows(src.ctypes.data, dst.ctypes.data, p, n, int(rows_per_head),
+                                    int(row_bytes)), "duo_reorder_head_rows")
+    return dst
 
 
 def head_permutation(mask: Sequence[int]):

@@ -2,7 +2,9 @@
 // dispatch to the kernel launchers. Every check runs before any HIP call, so
 // a failed call enqueues nothing and leaves the layer unchanged.
 #include <math.h>
+#include <algorithm>
 #include <new>
+#include <vector>
 #include <stdlib.h>
 #include <string.h>
 
@@ -309,6 +311,44 @@ duo_status duo_head_permutation(const uint8_t* mask, int32_t n, int32_t* perm,
   *n_retrieval = w;
   for (int32_t h = 0; h < n; ++h)
     if (!mask[h]) perm[w++] = h;
+  return DUO_OK;
+}
+
+duo_status duo_binarize_gates(const float* alpha, int32_t n, double sparsity, uint8_t* mask) {
+  if (!alpha || !mask || n < 1) return DUO_ERR_INVALID_ARG;
+  if (!(sparsity >= 0.0 && sparsity <= 1.0)) return DUO_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (isnan(alpha[i])) return DUO_ERR_INVALID_ARG;
+  const int64_t n_stream = (int64_t)floor(sparsity * (double)n);
+  if (n_stream >= n) {
+    memset(mask, 0, (size_t)n);
+    return DUO_OK;
+  }
+  std::vector<float> sorted(alpha, alpha + n);
+  std::nth_element(sorted.begin(), sorted.begin() + n_stream, sorted.end());
+  const float tau = sorted[(size_t)n_stream];
+  for (int32_t i = 0; i < n; ++i) mask[i] = alpha[i] >= tau ? 1 : 0;
+  return DUO_OK;
+}
+
+duo_status duo_reorder_head_rows(const void* in, void* out, const int32_t* perm, int32_t n_heads,
+                                 int64_t rows_per_head, int64_t row_bytes) {
+  if (!in || !out || !perm || n_heads < 1 || rows_per_head < 1 || row_bytes < 1)
+    return DUO_ERR_INVALID_ARG;
+  const size_t block = (size_t)rows_per_head * (size_t)row_bytes;
+  const size_t total = block * (size_t)n_heads;
+  if (block / (size_t)row_bytes != (size_t)rows_per_head || total / block != (size_t)n_heads)
+    return DUO_ERR_INVALID_ARG;
+  const char* src = static_cast<const char*>(in);
+  char* dst = static_cast<char*>(out);
+  if (src < dst + total && dst < src + total) return DUO_ERR_LAYOUT;  // overlapping buffers
+  std::vector<uint8_t> seen((size_t)n_heads, 0);
+  for (int32_t i = 0; i < n_heads; ++i) {
+    if (perm[i] < 0 || perm[i] >= n_heads || seen[(size_t)perm[i]]) return DUO_ERR_INVALID_ARG;
+    seen[(size_t)perm[i]] = 1;
+  }
+  for (int32_t i = 0; i < n_heads; ++i)
+    memcpy(dst + (size_t)i * block, src + (size_t)perm[i] * block, block);
   return DUO_OK;
 }
 

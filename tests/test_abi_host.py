@@ -171,6 +171,46 @@ def test_mixed_alpha_grad_workspace_and_validation():
     assert f(ctypes.byref(d), *args(T=big, ws_bytes=1 << 40), None) == 2
 
 
+def test_binarize_gates_matches_oracle_bit_for_bit():
+    from kv_cache_compression_duo_amd import binarize_gates
+    g = rng(52)
+    for _ in range(300):
+        n = int(g.integers(1, 300))
+        a = g.uniform(-0.2, 1.2, n).astype(np.float32)
+        if n > 3 and g.integers(0, 2):
+            a[: n // 3] = a[0]  # ties
+        s = float(g.choice([0.0, 1.0, g.uniform(0.0, 1.0), 0.29, 0.5]))
+        assert binarize_gates(a, s) == oracle.binarize_gates(a.astype(np.float64), s).tolist()
+    L = _lib()
+    a = (ctypes.c_float * 3)(0.1, float("nan"), 0.3)
+    m = (ctypes.c_uint8 * 3)()
+    assert L.lib.duo_binarize_gates(a, 3, 0.5, m) == 1
+    b = (ctypes.c_float * 3)(0.1, 0.2, 0.3)
+    assert L.lib.duo_binarize_gates(b, 3, -0.1, m) == 1
+    assert L.lib.duo_binarize_gates(b, 3, 1.5, m) == 1
+    assert L.lib.duo_binarize_gates(b, 0, 0.5, m) == 1
+
+
+def test_reorder_head_rows_matches_oracle_bit_for_bit():
+    from kv_cache_compression_duo_amd import reorder_head_rows
+    g = rng(53)
+    for dtype in (np.float32, np.uint16, np.float64):
+        n, rph, cols = 6, 4, 10
+        w = (g.standard_normal((n * rph, cols)) * 1000).astype(dtype)
+        perm = g.permutation(n)
+        np.testing.assert_array_equal(reorder_head_rows(w, perm, rph),
+                                      oracle.reorder_head_rows(w, perm, rph))
+    L = _lib()
+    src = np.arange(12, dtype=np.float32)
+    dst = np.zeros(12, np.float32)
+    bad = (ctypes.c_int32 * 3)(0, 0, 2)  # not a permutation
+    assert L.lib.duo_reorder_head_rows(src.ctypes.data, dst.ctypes.data, bad, 3, 1, 16) == 1
+    ok = (ctypes.c_int32 * 3)(2, 0, 1)
+    assert L.lib.duo_reorder_head_rows(src.ctypes.data, src.ctypes.data, ok, 3, 1, 16) == 3
+    assert L.lib.duo_reorder_head_rows(src.ctypes.data, dst.ctypes.data, ok, 3, 1, 16) == 0
+    np.testing.assert_array_equal(dst, np.concatenate([src[8:12], src[0:4], src[4:8]]))
+
+
 def test_status_strings():
     L = _lib()
     assert L.status_string(0) == "ok"
