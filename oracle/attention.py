@@ -20,17 +20,26 @@ Readings (the pages leave these open):
   * query head h reads KV head h // G (G = query heads per KV head).
 Masks are taken on absolute token positions, so a chunk or a ring cache is
 handled by passing the positions its rows hold.
+
+Block-sparse Lambda (the approximation used while training the gates --
+paperlayer summary, appendix A.1; its figure is missing from the pages):
+reading taken here, with block size b, query block i // b and key block
+j // b: key j is allowed when j <= i and (its block is one of the first
+ceil(S / b) blocks, or the query's block minus the key's block is below
+ceil(R / b)). b = 1 is the token-level Lambda mask.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def allowed_mask(q_pos, k_pos, kind: str, sink: int, recent: int) -> np.ndarray:
+def allowed_mask(q_pos, k_pos, kind: str, sink: int, recent: int, block: int = 0) -> np.ndarray:
     """Boolean [len(q_pos), len(k_pos)]: may query position i attend key j.
 
     full:      j <= i
     streaming: j <= i and (j < sink or i - j < recent)   (the Lambda mask)
+    streaming with block b > 0 (block-sparse Lambda):
+               j <= i and (j // b < ceil(sink / b) or i // b - j // b < ceil(recent / b))
     """
     i = np.asarray(q_pos, dtype=np.int64)[:, None]
     j = np.asarray(k_pos, dtype=np.int64)[None, :]
@@ -38,19 +47,23 @@ def allowed_mask(q_pos, k_pos, kind: str, sink: int, recent: int) -> np.ndarray:
     if kind == "full":
         return causal
     if kind == "streaming":
-        return causal & ((j < sink) | (i - j < recent))
+        if block <= 0:
+            return causal & ((j < sink) | (i - j < recent))
+        sink_blocks = -(-sink // block)
+        local_blocks = -(-recent // block)
+        return causal & ((j // block < sink_blocks) | (i // block - j // block < local_blocks))
     raise ValueError(kind)
 
 
 def masked_attention(q, k, v, q_pos, k_pos, scale: float, kind: str,
-                     sink: int = 16, recent: int = 64) -> np.ndarray:
+                     sink: int = 16, recent: int = 64, block: int = 0) -> np.ndarray:
     """o_i = sum_j p_ij v_j / sum_j p_ij over allowed j, p_ij = exp(s_ij - max_j s_ij),
     s_ij = scale * q_i . k_j.  q [Tq, D], k/v [Tk, D]; returns float64 [Tq, D]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     s = scale * (q @ k.T)
-    keep = allowed_mask(q_pos, k_pos, kind, sink, recent)
+    keep = allowed_mask(q_pos, k_pos, kind, sink, recent, block)
     if not keep.any(axis=1).all():
         raise ValueError("a query row has no allowed key")
     s = np.where(keep, s, -np.inf)
@@ -105,11 +118,12 @@ def streaming_attention(q, k, v, scale: float, sink: int = 16, recent: int = 64,
 
 
 def mixed_attention(q, k, v, alpha, scale: float, sink: int = 16, recent: int = 64,
-                    heads=None, rows=None) -> np.ndarray:
+                    heads=None, rows=None, block: int = 0) -> np.ndarray:
     """Gate-blended forward used for head identification:
     o_h = alpha[h // G] * full_h + (1 - alpha[h // G]) * streaming_h.
     q [T,Hq,D], k/v [T,Hkv,D], alpha [Hkv]; returns float64 [T,Hq,D].
-    ``heads`` / ``rows`` restrict the query heads / rows computed (others NaN)."""
+    ``heads`` / ``rows`` restrict the query heads / rows computed (others NaN);
+    ``block`` > 0 takes the streaming part under the block-sparse Lambda mask."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, D = q.shape
     Hkv = np.asarray(k).shape[1]
@@ -122,6 +136,6 @@ def mixed_attention(q, k, v, alpha, scale: float, sink: int = 16, recent: int = 
         a = float(alpha[kv])
         full = masked_attention(q[rows, h], k[:, kv], v[:, kv], rows, pos, scale, "full")
         stream = masked_attention(q[rows, h], k[:, kv], v[:, kv], rows, pos, scale,
-                                  "streaming", sink, recent)
+                                  "streaming", sink, recent, block)
         out[rows, h] = a * full + (1.0 - a) * stream
     return out

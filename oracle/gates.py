@@ -37,9 +37,10 @@ from .attention import masked_attention
 
 
 def mixed_alpha_grad(q, k, v, dout, alpha, scale: float, sink: int = 16, recent: int = 64,
-                     l1_weight: float = 0.0) -> np.ndarray:
+                     l1_weight: float = 0.0, block: int = 0) -> np.ndarray:
     """dL/dalpha for the gate-blended forward over one sequence.
     q [T,Hq,D], k/v [T,Hkv,D], dout [T,Hq,D] (dL_distill/do), alpha [Hkv];
+    ``block`` > 0 takes the streaming part under the block-sparse Lambda mask;
     returns float64 [Hkv]."""
     q = np.asarray(q, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -54,7 +55,7 @@ def mixed_alpha_grad(q, k, v, dout, alpha, scale: float, sink: int = 16, recent:
         kv = h // G
         full = masked_attention(q[:, h], k[:, kv], v[:, kv], pos, pos, scale, "full")
         stream = masked_attention(q[:, h], k[:, kv], v[:, kv], pos, pos, scale, "streaming",
-                                  sink, recent)
+                                  sink, recent, block)
         grad[kv] += float(np.sum(dout[:, h] * (full - stream)))
     grad += l1_weight * np.sign(np.asarray(alpha, dtype=np.float64))
     return grad
