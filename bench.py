@@ -320,6 +320,20 @@ def bench_prefill_llama3(args, dev):
             "mfma_frac_total": (ret_flops + str_flops) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def block_lambda_pairs(T, S, R, b):
+    """Allowed pairs of T queries (positions 0..T-1) under the block-sparse
+    Lambda mask: key j visible to query i when j <= i and (j // b <
+    ceil(S / b) or i // b - j // b < ceil(R / b))."""
+    sb, rb = -(-S // b), -(-R // b)
+    tot = 0
+    for qb in range(-(-T // b)):
+        for i in range(qb * b, min(T, qb * b + b)):
+            lo_local = max(0, (qb - rb + 1) * b)
+            sink_hi = min(sb * b, i + 1)
+            tot += sink_hi + max(0, i + 1 - max(lo_local, sink_hi))
+    return tot
+
+
 def bench_mixed(args, dev):
     import torch
     import kv_cache_compression_duo_amd as duo
@@ -337,8 +351,15 @@ def bench_mixed(args, dev):
     fn()
     ms = sorted(time_region(torch, fn) for _ in range(5))[2]
     flops = H * (causal_pairs(0, T) + lambda_pairs(0, T, w.sink, w.recent)) * 4 * D
+    # the block-sparse Lambda form used while training the gates (64-token blocks)
+    fb = lambda: duo.mixed_forward(q, k, v, alpha, softmax_scale=w.softmax_scale, out=out,  # noqa: E731
+                                   lambda_block=64)
+    fb()
+    ms_b = sorted(time_region(torch, fb) for _ in range(5))[2]
+    flops_b = H * (causal_pairs(0, T) + block_lambda_pairs(T, w.sink, w.recent, 64)) * 4 * D
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tflop": flops / 1e12,
-            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "block_sparse_ms": ms_b, "block_sparse_tflops": flops_b / (ms_b * 1e-3) / 1e12}
 
 
 def bench_mixed_alpha_grad(args, dev):

@@ -167,6 +167,17 @@ duo_status duo_mixed_forward(const duo_layer_desc* desc, const void* q, const vo
                              const void* v, const float* alpha, int32_t seq_len, void* out,
                              hipStream_t stream);
 
+/* duo_mixed_forward with the streaming part under the block-sparse Lambda
+ * mask used while training the gates (paperlayer summary of arXiv
+ * 2410.10819v1, appendix A.1; its figure is missing, the reading is stated
+ * here): with lambda_block = b = 64, query i may attend key j when j <= i and
+ * (j / b < ceil(sink / b) or i / b - j / b < ceil(recent / b)) (integer
+ * division). lambda_block = 0 is the token-level mask (duo_mixed_forward);
+ * other values return DUO_ERR_UNSUPPORTED. */
+duo_status duo_mixed_forward_block(const duo_layer_desc* desc, const void* q, const void* k,
+                                   const void* v, const float* alpha, int32_t seq_len,
+                                   int32_t lambda_block, void* out, hipStream_t stream);
+
 /* Workspace (device memory, 16-byte aligned) that duo_mixed_alpha_grad needs
  * for seq_len tokens: one fp32 partial sum per attention block. Returns 0 for
  * an invalid descriptor or seq_len < 1. */
@@ -201,6 +212,14 @@ duo_status duo_mixed_alpha_grad(const duo_layer_desc* desc, const void* q, const
  * heads. */
 duo_status duo_head_permutation(const uint8_t* mask, int32_t n_kv_heads, int32_t* perm_out,
                                 int32_t* n_retrieval_out);
+
+/* duo_mixed_alpha_grad with the block-sparse Lambda mask of
+ * duo_mixed_forward_block (lambda_block 0 or 64). */
+duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* desc, const void* q, const void* k,
+                                      const void* v, const void* dout, const float* alpha,
+                                      float l1_weight, int32_t seq_len, int32_t lambda_block,
+                                      float* grad_alpha, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* Host-only: retrieval mask from trained gates (xllm-io review, section 三
  * 检索头识别, step 3: alpha is binarized as 1[alpha >= tau]; paperlayer

@@ -63,6 +63,11 @@ def _load():
         "duo_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "duo_mixed_forward": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_int32, c_void_p, c_void_p]),
+        "duo_mixed_forward_block": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+        "duo_mixed_alpha_grad_block": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_void_p, c_float, c_int32, c_int32,
+                                               c_void_p, c_void_p, c_size_t, c_void_p]),
         "duo_mixed_alpha_grad_workspace": (c_size_t, [POINTER(LayerDesc), c_int32]),
         "duo_mixed_alpha_grad": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_float, c_int32, c_void_p,

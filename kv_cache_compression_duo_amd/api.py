@@ -165,9 +165,11 @@ def _bytes_view(buf: torch.Tensor, offset: int, shape, dtype) -> torch.Tensor:
 
 
 def mixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, *,
-                  softmax_scale: float, sink: int = 16, recent: int = 64, out=None):
+                  softmax_scale: float, sink: int = 16, recent: int = 64, out=None,
+                  lambda_block: int = 0):
     """out_h = alpha[h // G] * full_h + (1 - alpha[h // G]) * streaming_h.
-    q [B,T,Hq,D] bf16, k/v [B,T,Hkv,D] bf16, alpha [Hkv] fp32 (device)."""
+    q [B,T,Hq,D] bf16, k/v [B,T,Hkv,D] bf16, alpha [Hkv] fp32 (device).
+    lambda_block = 64 takes the streaming part under the block-sparse mask."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     _check_act(q, "q", (B, T, Hq, D), torch.bfloat16)
@@ -179,14 +181,16 @@ def mixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     _check_act(out, "out", (B, T, Hq, D), torch.bfloat16)
     desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
                      sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
-    check(lib.duo_mixed_forward(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), T,
-                                _ptr(out), _stream_ptr(q.device)), "duo_mixed_forward")
+    check(lib.duo_mixed_forward_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), T,
+                                      int(lambda_block), _ptr(out), _stream_ptr(q.device)),
+          "duo_mixed_forward_block")
     return out
 
 
 def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
                      alpha: torch.Tensor, *, softmax_scale: float, sink: int = 16,
-                     recent: int = 64, l1_weight: float = 0.0, grad=None, workspace=None):
+                     recent: int = 64, l1_weight: float = 0.0, grad=None, workspace=None,
+                     lambda_block: int = 0):
     """Gradient with respect to the gates of mixed_forward:
     grad[kv] = sum of dout * (full - streaming) over the batch, tokens, the
     query heads of KV head kv and channels, + l1_weight * sign(alpha[kv]).
@@ -207,10 +211,11 @@ def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: to
     need = int(lib.duo_mixed_alpha_grad_workspace(byref(desc), T))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    check(lib.duo_mixed_alpha_grad(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-                                   _ptr(alpha), float(l1_weight), T, _ptr(grad),
-                                   _ptr(workspace), workspace.numel(), _stream_ptr(q.device)),
-          "duo_mixed_alpha_grad")
+    check(lib.duo_mixed_alpha_grad_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                         _ptr(alpha), float(l1_weight), T, int(lambda_block),
+                                         _ptr(grad), _ptr(workspace), workspace.numel(),
+                                         _stream_ptr(q.device)),
+          "duo_mixed_alpha_grad_block")
     return grad
 
 

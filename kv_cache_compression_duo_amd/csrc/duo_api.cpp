@@ -255,12 +255,13 @@ duo_status duo_decode(duo_layer* L, const void* q, const void* k_new, const void
   return DUO_OK;
 }
 
-duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void* k,
-                             const void* v, const float* alpha, int32_t T, void* out,
-                             hipStream_t stream) {
+duo_status duo_mixed_forward_block(const duo_layer_desc* d, const void* q, const void* k,
+                                   const void* v, const float* alpha, int32_t T,
+                                   int32_t lambda_block, void* out, hipStream_t stream) {
   duo_status st = check_desc(d);
   if (st != DUO_OK) return st;
   if (d->kv_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (lambda_block != 0 && lambda_block != 64) return DUO_ERR_UNSUPPORTED;
   if (T < 1) return DUO_ERR_INVALID_ARG;
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
@@ -270,8 +271,15 @@ duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void*
   // the kernel reads one KV head's rows of a sequence through a 32-bit range
   if ((int64_t)T * d->n_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
     return DUO_ERR_UNSUPPORTED;
-  if (launch_mixed(*d, q, k, v, alpha, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
+  if (launch_mixed(*d, q, k, v, alpha, T, lambda_block, out, stream) != hipSuccess)
+    return DUO_ERR_HIP;
   return DUO_OK;
+}
+
+duo_status duo_mixed_forward(const duo_layer_desc* d, const void* q, const void* k,
+                             const void* v, const float* alpha, int32_t T, void* out,
+                             hipStream_t stream) {
+  return duo_mixed_forward_block(d, q, k, v, alpha, T, 0, out, stream);
 }
 
 size_t duo_mixed_alpha_grad_workspace(const duo_layer_desc* d, int32_t T) {
@@ -279,13 +287,15 @@ size_t duo_mixed_alpha_grad_workspace(const duo_layer_desc* d, int32_t T) {
   return align_up(mixed_grad_partials(*d, T) * sizeof(float), 256);
 }
 
-duo_status duo_mixed_alpha_grad(const duo_layer_desc* d, const void* q, const void* k,
-                                const void* v, const void* dout, const float* alpha,
-                                float l1_weight, int32_t T, float* grad, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* d, const void* q, const void* k,
+                                      const void* v, const void* dout, const float* alpha,
+                                      float l1_weight, int32_t T, int32_t lambda_block,
+                                      float* grad, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
   duo_status st = check_desc(d);
   if (st != DUO_OK) return st;
   if (d->kv_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (lambda_block != 0 && lambda_block != 64) return DUO_ERR_UNSUPPORTED;
   if (T < 1 || !isfinite(l1_weight)) return DUO_ERR_INVALID_ARG;
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(dout)) != DUO_OK)
@@ -293,13 +303,20 @@ duo_status duo_mixed_alpha_grad(const duo_layer_desc* d, const void* q, const vo
   if (!alpha || !grad || !ws) return DUO_ERR_INVALID_ARG;
   if (!aligned(alpha, 4) || !aligned(grad, 4) || !aligned(ws, 16)) return DUO_ERR_LAYOUT;
   if (ws_bytes < mixed_grad_partials(*d, T) * sizeof(float)) return DUO_ERR_INVALID_ARG;
-  // the kernel reads one KV head's rows of a sequence through a 32-bit range
   if ((int64_t)T * d->n_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
     return DUO_ERR_UNSUPPORTED;
-  if (launch_mixed_alpha_grad(*d, q, k, v, dout, alpha, l1_weight, T, grad,
+  if (launch_mixed_alpha_grad(*d, q, k, v, dout, alpha, l1_weight, T, lambda_block, grad,
                               static_cast<float*>(ws), stream) != hipSuccess)
     return DUO_ERR_HIP;
   return DUO_OK;
+}
+
+duo_status duo_mixed_alpha_grad(const duo_layer_desc* d, const void* q, const void* k,
+                                const void* v, const void* dout, const float* alpha,
+                                float l1_weight, int32_t T, float* grad, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return duo_mixed_alpha_grad_block(d, q, k, v, dout, alpha, l1_weight, T, 0, grad, ws,
+                                    ws_bytes, stream);
 }
 
 duo_status duo_head_permutation(const uint8_t* mask, int32_t n, int32_t* perm,

@@ -56,14 +56,14 @@ hipError_t launch_prefill_retrieval(const duo_layer* L, const void* q, int T, vo
 hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const void* k,
                                     const void* v, int T, void* out, hipStream_t s);
 hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, const void* v,
-                        const float* alpha, int T, void* out, hipStream_t s);
+                        const float* alpha, int T, int lam_block, void* out, hipStream_t s);
 // gate gradient of the gate-blended forward: partial sums per flash block
 // (mixed_grad_partials floats), then one reduction launch
 size_t mixed_grad_partials(const duo_layer_desc& d, int T);
 hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const void* k,
                                    const void* v, const void* dout, const float* alpha,
-                                   float l1_weight, int T, float* grad, float* partial,
-                                   hipStream_t s);
+                                   float l1_weight, int T, int lam_block, float* grad,
+                                   float* partial, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace duo

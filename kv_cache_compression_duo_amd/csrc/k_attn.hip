@@ -45,7 +45,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum { MODE_RETRIEVAL = 0, MODE_STREAMING = 1, MODE_MIXED = 2, MODE_GRAD = 3 };
+// Kernel modes; the _BLOCK variants take the streaming part of the
+// two-phase modes under the block-sparse Lambda mask.
+enum {
+  MODE_RETRIEVAL = 0,
+  MODE_STREAMING = 1,
+  MODE_MIXED = 2,
+  MODE_GRAD = 3,
+  MODE_MIXED_BLOCK = 4,
+  MODE_GRAD_BLOCK = 5
+};
 
 struct AttnArgs {
   const uint16_t* q;     // [B][T][Hq][D]
@@ -131,8 +140,9 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   constexpr int BMT = TOKW * NW / HB;  // tokens per block
   constexpr int KPAD = D + 8;         // K tile row stride in LDS (elements)
   constexpr int KLD = D / 32;         // 16-byte K loads per thread
-  constexpr bool kMixed = MODE == MODE_MIXED;
-  constexpr bool kGrad = MODE == MODE_GRAD;
+  constexpr bool kMixed = MODE == MODE_MIXED || MODE == MODE_MIXED_BLOCK;
+  constexpr bool kGrad = MODE == MODE_GRAD || MODE == MODE_GRAD_BLOCK;
+  constexpr bool kBlock = MODE == MODE_MIXED_BLOCK || MODE == MODE_GRAD_BLOCK;
   // the gate-blended forward and its gate gradient visit the Lambda tiles,
   // then all causal tiles
   constexpr bool kTwoPhase = kMixed || kGrad;
@@ -172,9 +182,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // phase 1 of the mixed forward; the causal tiles follow (retrieval mode,
   // phase 2 of the mixed forward).
   int n1 = 0, w0 = 0, nlam = 0, ntiles;
+  // block-sparse Lambda (64-token blocks, the key tile): a key block is
+  // visible when among the first sbk blocks or within rbk blocks of the
+  // query's block
+  constexpr bool lblk = kBlock;
+  const int sbk = (a.S + kBN - 1) / kBN, rbk = (a.R + kBN - 1) / kBN;
   if constexpr (MODE != MODE_RETRIEVAL) {
-    const int lo = i_min - a.R + 1 > 0 ? i_min - a.R + 1 : 0;
-    const int sink_hi = a.S < i_max + 1 ? a.S : i_max + 1;
+    const int lo0 = lblk ? (i_min / kBN - rbk + 1) * kBN : i_min - a.R + 1;
+    const int lo = lo0 > 0 ? lo0 : 0;
+    const int s_eff = lblk ? sbk * kBN : a.S;
+    const int sink_hi = s_eff < i_max + 1 ? s_eff : i_max + 1;
     n1 = (sink_hi + kBN - 1) / kBN;  // sink tiles cover [0, 64*n1)
     w0 = lo > kBN * n1 ? lo : kBN * n1;
     const int n2 = i_max >= w0 ? (i_max - w0) / kBN + 1 : 0;
@@ -435,7 +452,9 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
             const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
             // bitwise operators: a select per element, no per-lane branches
             const bool causal = jp <= i_q;
-            const bool lam = causal & ((jp < a.S) | (i_q - jp < a.R));
+            const bool lam =
+                causal & (lblk ? (((jp >> 6) < sbk) | (((i_q >> 6) - (jp >> 6)) < rbk))
+                               : ((jp < a.S) | (i_q - jp < a.R)));
             st[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
           }
       }
@@ -609,7 +628,7 @@ hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const voi
 }
 
 hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, const void* v,
-                        const float* alpha, int T, void* out, hipStream_t s) {
+                        const float* alpha, int T, int lam_block, void* out, hipStream_t s) {
   AttnArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
@@ -625,7 +644,8 @@ hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, c
   a.n = 0;
   a.kv_base = 0;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  return launch_mode<MODE_MIXED>(a, d.head_dim, d.n_kv_heads, d.batch, s);
+  return lam_block ? launch_mode<MODE_MIXED_BLOCK>(a, d.head_dim, d.n_kv_heads, d.batch, s)
+                   : launch_mode<MODE_MIXED>(a, d.head_dim, d.n_kv_heads, d.batch, s);
 }
 
 // Gate gradient: the flash pass writes one partial sum per block; this
@@ -666,8 +686,8 @@ size_t mixed_grad_partials(const duo_layer_desc& d, int T) {
 
 hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const void* k,
                                    const void* v, const void* dout, const float* alpha,
-                                   float l1_weight, int T, float* grad, float* partial,
-                                   hipStream_t s) {
+                                   float l1_weight, int T, int lam_block, float* grad,
+                                   float* partial, hipStream_t s) {
   AttnArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
   a.k_in = static_cast<const uint16_t*>(k);
@@ -684,7 +704,9 @@ hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const
   a.n = 0;
   a.kv_base = 0;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  hipError_t e = launch_mode<MODE_GRAD>(a, d.head_dim, d.n_kv_heads, d.batch, s);
+  hipError_t e = lam_block
+                     ? launch_mode<MODE_GRAD_BLOCK>(a, d.head_dim, d.n_kv_heads, d.batch, s)
+                     : launch_mode<MODE_GRAD>(a, d.head_dim, d.n_kv_heads, d.batch, s);
   if (e != hipSuccess) return e;
   const int HB = heads_per_block(a.G), BMT = 32 * 8 / HB;
   const int per_kv = (a.G / HB) * ((T + BMT - 1) / BMT);

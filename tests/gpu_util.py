@@ -81,3 +81,42 @@ class Routed:
 
     def out(self, t):
         return t.index_select(-2, self.q_inv.to(t.device)).contiguous()
+
+
+def grad_tolerance(q, k, v, dout, scale, S, R, block=0):
+    """Per-KV-head bound on |g_gpu - g_ref| for the gate gradient from the
+    bf16 rounding of the softmax weights (relative error <= 2^-9 per weight,
+    row sums over the same rounded values). To first order a weight error
+    e_tj moves the gradient by w_tj * e_tj * dout_t . (v_j - o_t); the
+    roundings are independent, so by Hoeffding's inequality the total stays
+    within 6 * 2^-9 * sqrt(sum (w_tj * dout_t . (v_j - o_t))^2) over both
+    attentions (exceeded with probability below 1e-7); 1e-5 of
+    sum |dout * o| is added for fp32 accumulation. ``block`` > 0 takes the
+    streaming mask block-sparse (64-token blocks in the kernel)."""
+    q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    pos = np.arange(T)
+    i, j = pos[:, None], pos[None, :]
+    causal = j <= i
+    if block:
+        sb, rb = -(-S // block), -(-R // block)
+        lam = causal & ((j // block < sb) | (i // block - j // block < rb))
+    else:
+        lam = causal & ((j < S) | (i - j < R))
+    var = np.zeros(Hkv)
+    mass = np.zeros(Hkv)
+    for h in range(Hq):
+        kv = h // G
+        s = scale * q[:, h] @ k[:, kv].T
+        for allowed in (causal, lam):
+            z = np.where(allowed, s, -np.inf)
+            z -= z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            w /= w.sum(axis=1, keepdims=True)
+            o = w @ v[:, kv]
+            dv = dout[:, h] @ v[:, kv].T - np.sum(dout[:, h] * o, axis=1, keepdims=True)
+            var[kv] += np.sum((w * dv) ** 2)
+            mass[kv] += np.sum(np.abs(dout[:, h] * o))
+    return 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass

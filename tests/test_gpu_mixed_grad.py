@@ -26,35 +26,9 @@ import torch
 
 import oracle
 from duo_synth import WORKLOADS, device_normal, normal, random_case, rng, round_bf16
-from gpu_util import device, say, to_dev
+from gpu_util import device, grad_tolerance, say, to_dev
 
 pytestmark = pytest.mark.gpu
-
-
-def _tolerance(q, k, v, dout, scale, S, R):
-    """Per-KV-head bound on |g_gpu - g_ref| from the bf16 rounding of P."""
-    q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
-    T, Hq, D = q.shape
-    Hkv = k.shape[1]
-    G = Hq // Hkv
-    pos = np.arange(T)
-    causal = pos[None, :] <= pos[:, None]
-    lam = causal & ((pos[None, :] < S) | (pos[:, None] - pos[None, :] < R))
-    var = np.zeros(Hkv)
-    mass = np.zeros(Hkv)
-    for h in range(Hq):
-        kv = h // G
-        s = scale * q[:, h] @ k[:, kv].T
-        for allowed in (causal, lam):
-            z = np.where(allowed, s, -np.inf)
-            z -= z.max(axis=1, keepdims=True)
-            w = np.exp(z)
-            w /= w.sum(axis=1, keepdims=True)
-            o = w @ v[:, kv]
-            dv = dout[:, h] @ v[:, kv].T - np.sum(dout[:, h] * o, axis=1, keepdims=True)
-            var[kv] += np.sum((w * dv) ** 2)
-            mass[kv] += np.sum(np.abs(dout[:, h] * o))
-    return 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass
 
 
 def _case(seed, T, Hq, Hkv, D, alpha):
@@ -90,7 +64,7 @@ def test_alpha_grad_matches_oracle(T, Hq, Hkv, D, S, R):
     say(f"case: alpha grad T={T} Hq={Hq} Hkv={Hkv} D={D} S={S} R={R}")
     got = _gpu_grad([q], [k], [v], [dout], alpha, scale, S, R, l1)
     ref = oracle.mixed_alpha_grad(q, k, v, dout, alpha, scale, S, R, l1_weight=l1)
-    tol = _tolerance(q, k, v, dout, scale, S, R)
+    tol = grad_tolerance(q, k, v, dout, scale, S, R)
     say(f"  max |got - ref| = {np.abs(got - ref).max():.3e}, min tolerance {tol.min():.3e}, "
         f"max |ref| = {np.abs(ref).max():.3e}")
     assert np.all(np.abs(got - ref) <= tol), (got, ref, tol)
@@ -107,7 +81,7 @@ def test_alpha_grad_batch_of_two():
                     [c[3] for c in cases], alpha, scale, S, R, l1)
     ref = sum(oracle.mixed_alpha_grad(c[0], c[1], c[2], c[3], alpha, scale, S, R)
               for c in cases) + l1 * np.sign(alpha)
-    tol = sum(_tolerance(c[0], c[1], c[2], c[3], scale, S, R) for c in cases)
+    tol = sum(grad_tolerance(c[0], c[1], c[2], c[3], scale, S, R) for c in cases)
     assert np.all(np.abs(got - ref) <= tol), (got, ref, tol)
 
 
