@@ -125,17 +125,34 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* desc, void* ret
                           void* streaming_buf, void* workspace, int64_t n_tokens_existing,
                           hipStream_t stream);
 
+/* As duo_layer_init, for a batch whose sequences already hold different
+ * token counts: n_tokens_existing[batch] (each within the capacity). Such a
+ * ragged layer (batch <= 64; larger ragged batches return
+ * DUO_ERR_UNSUPPORTED) decodes every sequence at its own position and grows
+ * its sequences one at a time with duo_append_kv_seq / duo_prefill_chunk_seq
+ * (serving: sequences admitted at different times; paperlayer summary of
+ * arXiv 2410.10819v1, section 4, and xllm-io review, section 三 推理流程). */
+duo_status duo_layer_init_ragged(duo_layer** out, const duo_layer_desc* desc, void* retrieval_buf,
+                                 void* streaming_buf, void* workspace,
+                                 const int64_t* n_tokens_existing, hipStream_t stream);
+
 /* Free the host object (never the caller's buffers). Null is accepted. */
 duo_status duo_layer_destroy(duo_layer* layer);
 
-/* Tokens currently cached by the layer (host counter), or -1 for null. */
+/* Tokens currently cached by the layer (host counter): the largest count over
+ * the batch's sequences, or -1 for null. */
 int64_t duo_layer_tokens(const duo_layer* layer);
+
+/* Tokens cached by sequence b, or -1 for null or b outside [0, batch). */
+int64_t duo_layer_sequence_tokens(const duo_layer* layer, int32_t b);
 
 /* Append `n_tokens` >= 1 tokens of K/V ([B, n_tokens, Hkv, D], kv_dtype)
  * at positions [n, n + n_tokens) without attending: retrieval heads write
  * their cache rows (quantising them for INT4_G32), streaming heads write the
  * ring slots of the positions that survive (the sinks and the last `recent`).
- * Used to fill a context. DUO_ERR_CAPACITY if n + n_tokens > capacity. */
+ * Used to fill a context. DUO_ERR_CAPACITY if n + n_tokens > capacity;
+ * DUO_ERR_UNSUPPORTED while the sequences hold different counts (use
+ * duo_append_kv_seq). */
 duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t n_tokens,
                          hipStream_t stream);
 
@@ -146,16 +163,33 @@ duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t
  * as it was before the chunk plus the chunk, then the ring is updated.
  * Writes out [B, chunk_len, Hq, D] bf16 and advances the token count.
  * Layers whose kv_dtype or retrieval_dtype is not BF16 return
- * DUO_ERR_UNSUPPORTED (fill such caches with duo_append_kv). */
+ * DUO_ERR_UNSUPPORTED (fill such caches with duo_append_kv); so does a layer
+ * whose sequences hold different counts (use duo_prefill_chunk_seq). */
 duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,
                              int32_t chunk_len, void* out, hipStream_t stream);
 
 /* One decode step at position n: q [B, 1, Hq, D] bf16, k_new/v_new
  * [B, 1, Hkv, D]. The new token is appended to both caches, then every head
  * attends (retrieval: positions [0, n]; streaming: the sinks and the last
- * `recent` positions, the new one included). Writes out [B, 1, Hq, D] bf16. */
+ * `recent` positions, the new one included). Writes out [B, 1, Hq, D] bf16.
+ * Each sequence decodes at its own position n_b when the counts differ.
+ * DUO_ERR_CAPACITY if the longest sequence is full. */
 duo_status duo_decode(duo_layer* layer, const void* q, const void* k_new, const void* v_new,
                       void* out, hipStream_t stream);
+
+/* duo_append_kv for sequence b alone: k/v [1, n_tokens, Hkv, D] at its
+ * positions [n_b, n_b + n_tokens). DUO_ERR_INVALID_ARG for b outside
+ * [0, batch) or n_tokens < 1, DUO_ERR_CAPACITY if it would pass the
+ * capacity, DUO_ERR_UNSUPPORTED for batches above 64. */
+duo_status duo_append_kv_seq(duo_layer* layer, int32_t b, const void* k, const void* v,
+                             int32_t n_tokens, hipStream_t stream);
+
+/* duo_prefill_chunk for sequence b alone: q [1, chunk_len, Hq, D], k/v
+ * [1, chunk_len, Hkv, D], out [1, chunk_len, Hq, D], at its positions
+ * [n_b, n_b + chunk_len). Errors as for duo_append_kv_seq and
+ * duo_prefill_chunk. */
+duo_status duo_prefill_chunk_seq(duo_layer* layer, int32_t b, const void* q, const void* k,
+                                 const void* v, int32_t chunk_len, void* out, hipStream_t stream);
 
 /* Stateless gate-blended forward used for head identification:
  * out_h = alpha[h/G] * full_h + (1 - alpha[h/G]) * streaming_h over one

@@ -55,8 +55,14 @@ def _load():
         "duo_layer_layout": (c_int, [POINTER(LayerDesc), POINTER(Layout)]),
         "duo_layer_init": (c_int, [POINTER(c_void_p), POINTER(LayerDesc), c_void_p, c_void_p,
                                    c_void_p, c_int64, c_void_p]),
+        "duo_layer_init_ragged": (c_int, [POINTER(c_void_p), POINTER(LayerDesc), c_void_p,
+                                          c_void_p, c_void_p, POINTER(c_int64), c_void_p]),
         "duo_layer_destroy": (c_int, [c_void_p]),
         "duo_layer_tokens": (c_int64, [c_void_p]),
+        "duo_layer_sequence_tokens": (c_int64, [c_void_p, c_int32]),
+        "duo_append_kv_seq": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
+        "duo_prefill_chunk_seq": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                          c_void_p, c_void_p]),
         "duo_append_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
         "duo_prefill_chunk": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p]),

@@ -9,7 +9,7 @@ forward. ``head_permutation`` and ``ring_slot`` are the host helpers.
 from __future__ import annotations
 
 import ctypes
-from ctypes import POINTER, byref, c_float, c_int32, c_uint8, c_void_p
+from ctypes import POINTER, byref, c_float, c_int32, c_int64, c_uint8, c_void_p
 from typing import Optional, Sequence
 
 import torch
@@ -50,7 +50,9 @@ class DuoLayer:
                  n_retrieval_kv_heads: int, capacity: int, softmax_scale: float,
                  sink: int = 16, recent: int = 64, batch: int = 1, kv_dtype: str = "bf16",
                  retrieval_dtype: Optional[str] = None, device="cuda",
-                 n_tokens_existing: int = 0):
+                 n_tokens_existing=0):
+        """n_tokens_existing: one count for every sequence, or a list of
+        per-sequence counts (a ragged batch)."""
         self.desc = make_desc(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                               head_dim=head_dim, n_retrieval_kv_heads=n_retrieval_kv_heads,
                               sink=sink, recent=recent, capacity=capacity, kv_dtype=kv_dtype,
@@ -68,9 +70,17 @@ class DuoLayer:
         self.sbuf = torch.zeros(max(lay.streaming_bytes, 256), dtype=torch.uint8, device=self.device)
         self.ws = torch.zeros(max(lay.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
         h = c_void_p()
-        check(lib.duo_layer_init(byref(h), byref(self.desc), _ptr(self.rbuf), _ptr(self.sbuf),
-                                 _ptr(self.ws), n_tokens_existing, _stream_ptr(self.device)),
-              "duo_layer_init")
+        if isinstance(n_tokens_existing, (list, tuple)):
+            if len(n_tokens_existing) != batch:
+                raise ValueError("n_tokens_existing needs one count per sequence")
+            counts = (c_int64 * batch)(*[int(x) for x in n_tokens_existing])
+            check(lib.duo_layer_init_ragged(byref(h), byref(self.desc), _ptr(self.rbuf),
+                                            _ptr(self.sbuf), _ptr(self.ws), counts,
+                                            _stream_ptr(self.device)), "duo_layer_init_ragged")
+        else:
+            check(lib.duo_layer_init(byref(h), byref(self.desc), _ptr(self.rbuf), _ptr(self.sbuf),
+                                     _ptr(self.ws), int(n_tokens_existing),
+                                     _stream_ptr(self.device)), "duo_layer_init")
         self._h = h
 
     def close(self):
@@ -86,7 +96,11 @@ class DuoLayer:
 
     @property
     def n_tokens(self) -> int:
+        """Tokens cached: the largest count over the batch's sequences."""
         return int(lib.duo_layer_tokens(self._h))
+
+    def sequence_tokens(self, b: int) -> int:
+        return int(lib.duo_layer_sequence_tokens(self._h, int(b)))
 
     # -- calls -----------------------------------------------------------------
     def append_kv(self, k: torch.Tensor, v: torch.Tensor):
@@ -108,6 +122,29 @@ class DuoLayer:
         _check_act(out, "out", (self.B, T, self.Hq, self.D), torch.bfloat16)
         check(lib.duo_prefill_chunk(self._h, _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
                                     _stream_ptr(self.device)), "duo_prefill_chunk")
+        return out
+
+    def append_kv_seq(self, b: int, k: torch.Tensor, v: torch.Tensor):
+        """Append to sequence b alone: k/v [1, T, Hkv, D]."""
+        T = k.shape[1]
+        kvt = _TORCH[self.kv_dtype]
+        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt)
+        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt)
+        check(lib.duo_append_kv_seq(self._h, int(b), _ptr(k), _ptr(v), T,
+                                    _stream_ptr(self.device)), "duo_append_kv_seq")
+
+    def prefill_chunk_seq(self, b: int, q, k, v, out=None):
+        """Prefill a chunk of sequence b alone: q [1, T, Hq, D], k/v [1, T, Hkv, D]."""
+        T = q.shape[1]
+        kvt = _TORCH[self.kv_dtype]
+        _check_act(q, "q", (1, T, self.Hq, self.D), torch.bfloat16)
+        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt)
+        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt)
+        if out is None:
+            out = torch.empty_like(q)
+        _check_act(out, "out", (1, T, self.Hq, self.D), torch.bfloat16)
+        check(lib.duo_prefill_chunk_seq(self._h, int(b), _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
+                                        _stream_ptr(self.device)), "duo_prefill_chunk_seq")
         return out
 
     def decode(self, q, k, v, out=None):

@@ -145,16 +145,24 @@ duo_status duo_layer_layout(const duo_layer_desc* d, duo_layout* out) {
   return DUO_OK;
 }
 
-duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrieval_buf,
-                          void* streaming_buf, void* workspace, int64_t n_tokens_existing,
-                          hipStream_t stream) {
+static duo_status layer_init(duo_layer** out, const duo_layer_desc* d, void* retrieval_buf,
+                             void* streaming_buf, void* workspace, const int64_t* n_existing,
+                             int64_t n_uniform, hipStream_t stream) {
   if (!out) return DUO_ERR_INVALID_ARG;
   duo_layout lay;
   duo_status st = duo_layer_layout(d, &lay);
   if (st != DUO_OK) return st;
-  if (n_tokens_existing < 0) return DUO_ERR_INVALID_ARG;
-  if (d->n_retrieval_kv_heads > 0 && n_tokens_existing > d->retrieval_capacity)
-    return DUO_ERR_CAPACITY;
+  int64_t n_max = 0;
+  bool ragged = false;
+  for (int32_t b = 0; b < d->batch; ++b) {
+    const int64_t nb = n_existing ? n_existing[b] : n_uniform;
+    if (nb < 0) return DUO_ERR_INVALID_ARG;
+    if (d->n_retrieval_kv_heads > 0 && nb > d->retrieval_capacity) return DUO_ERR_CAPACITY;
+    if (nb > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
+    if (b > 0 && nb != n_max) ragged = true;
+    if (b == 0 || nb > n_max) n_max = nb;
+  }
+  if (ragged && d->batch > kMaxRaggedBatch) return DUO_ERR_UNSUPPORTED;
   if (lay.retrieval_bytes && !retrieval_buf) return DUO_ERR_INVALID_ARG;
   if (lay.streaming_bytes && !streaming_buf) return DUO_ERR_INVALID_ARG;
   if (!workspace) return DUO_ERR_INVALID_ARG;
@@ -162,12 +170,19 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrie
     return DUO_ERR_LAYOUT;
   duo_layer* L = new (std::nothrow) duo_layer;
   if (!L) return DUO_ERR_INVALID_ARG;
+  L->nseq = new (std::nothrow) int64_t[(size_t)d->batch];
+  if (!L->nseq) {
+    delete L;
+    return DUO_ERR_INVALID_ARG;
+  }
+  for (int32_t b = 0; b < d->batch; ++b) L->nseq[b] = n_existing ? n_existing[b] : n_uniform;
+  L->n = n_max;
+  L->ragged = ragged;
   L->d = *d;
   L->lay = lay;
   L->rbuf = static_cast<char*>(retrieval_buf);
   L->sbuf = static_cast<char*>(streaming_buf);
   L->ws = static_cast<char*>(workspace);
-  L->n = n_tokens_existing;
   L->G = d->n_q_heads / d->n_kv_heads;
   L->Hr = d->n_retrieval_kv_heads;
   L->Hs = d->n_kv_heads - d->n_retrieval_kv_heads;
@@ -179,6 +194,7 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrie
       L->cus <= 0)
     L->cus = 256;
   if (launch_zero(workspace, lay.workspace_bytes, stream) != hipSuccess) {
+    delete[] L->nseq;
     delete L;
     return DUO_ERR_HIP;
   }
@@ -186,12 +202,33 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrie
   return DUO_OK;
 }
 
+duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* d, void* retrieval_buf,
+                          void* streaming_buf, void* workspace, int64_t n_tokens_existing,
+                          hipStream_t stream) {
+  return layer_init(out, d, retrieval_buf, streaming_buf, workspace, nullptr, n_tokens_existing,
+                    stream);
+}
+
+duo_status duo_layer_init_ragged(duo_layer** out, const duo_layer_desc* d, void* retrieval_buf,
+                                 void* streaming_buf, void* workspace,
+                                 const int64_t* n_tokens_existing, hipStream_t stream) {
+  if (!n_tokens_existing) return DUO_ERR_INVALID_ARG;
+  return layer_init(out, d, retrieval_buf, streaming_buf, workspace, n_tokens_existing, 0,
+                    stream);
+}
+
 duo_status duo_layer_destroy(duo_layer* L) {
+  if (L) delete[] L->nseq;
   delete L;
   return DUO_OK;
 }
 
 int64_t duo_layer_tokens(const duo_layer* L) { return L ? L->n : -1; }
+
+int64_t duo_layer_sequence_tokens(const duo_layer* L, int32_t b) {
+  if (!L || b < 0 || b >= L->d.batch) return -1;
+  return L->nseq[b];
+}
 
 static duo_status check_act(const void* p) {
   if (!p) return DUO_ERR_INVALID_ARG;
@@ -199,15 +236,26 @@ static duo_status check_act(const void* p) {
   return DUO_OK;
 }
 
+// Every sequence grew by T tokens.
+static void advance_all(duo_layer* L, int64_t T) {
+  for (int32_t b = 0; b < L->d.batch; ++b) L->nseq[b] += T;
+  L->n += T;
+}
+
+static duo_status prefill_launch(duo_layer* L, const void* q, const void* k, const void* v,
+                                 int32_t T, void* out, hipStream_t stream);
+
 duo_status duo_append_kv(duo_layer* L, const void* k, const void* v, int32_t T,
                          hipStream_t stream) {
   if (!L || T < 1) return DUO_ERR_INVALID_ARG;
   duo_status st;
   if ((st = check_act(k)) != DUO_OK || (st = check_act(v)) != DUO_OK) return st;
+  if (L->ragged) return DUO_ERR_UNSUPPORTED;  // per sequence: duo_append_kv_seq
   if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
+  if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
   if (L->Hr > 0 && launch_append_cache(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
   if (L->Hs > 0 && launch_append_ring(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
-  L->n += T;
+  advance_all(L, T);
   return DUO_OK;
 }
 
@@ -219,8 +267,15 @@ duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const v
       (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
     return st;
   if (L->d.kv_dtype != DUO_BF16 || L->d.retrieval_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  if (L->ragged) return DUO_ERR_UNSUPPORTED;  // per sequence: duo_prefill_chunk_seq
   if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
+  return prefill_launch(L, q, k, v, T, out, stream);
+}
+
+// The batch-wide prefill of a (view of a) layer, after validation.
+static duo_status prefill_launch(duo_layer* L, const void* q, const void* k, const void* v,
+                                 int32_t T, void* out, hipStream_t stream) {
   // Retrieval heads: append the chunk, then attend causally over the cache.
   if (L->Hr > 0) {
     if (launch_append_cache(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
@@ -232,7 +287,7 @@ duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const v
     if (launch_prefill_streaming(L, q, k, v, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
     if (launch_append_ring(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
   }
-  L->n += T;
+  advance_all(L, T);
   return DUO_OK;
 }
 
@@ -251,7 +306,86 @@ duo_status duo_decode(duo_layer* L, const void* q, const void* k_new, const void
   else
     e = launch_decode(L, q, k_new, v_new, out, stream);
   if (e != hipSuccess) return DUO_ERR_HIP;
-  L->n += 1;
+  advance_all(L, 1);
+  return DUO_OK;
+}
+
+// A batch-1 view of sequence b of a layer: the same buffers at that
+// sequence's offsets (every array is laid out batch-major) and its count.
+static duo_layer sequence_view(const duo_layer* L, int32_t b) {
+  duo_layer v = *L;
+  const duo_layer_desc& d = L->d;
+  const size_t D = (size_t)d.head_dim, Hr = (size_t)L->Hr, Hs = (size_t)L->Hs;
+  const size_t W = (size_t)(d.sink + d.recent), bb = (size_t)b;
+  if (d.retrieval_dtype == DUO_INT4_G32) {
+    const size_t cap32 = (size_t)cap32_of(d.retrieval_capacity);
+    const size_t codes = Hr * cap32 * (D / 2), sz = Hr * cap32 * (D / 32) * 4;
+    v.lay.k_offset += bb * codes;
+    v.lay.v_offset += bb * codes;
+    v.lay.k_sz_offset += bb * sz;
+    v.lay.v_sz_offset += bb * sz;
+  } else {
+    const size_t arr = Hr * (size_t)d.retrieval_capacity * D * 2;
+    v.lay.k_offset += bb * arr;
+    v.lay.v_offset += bb * arr;
+  }
+  const size_t ring = Hs * W * D * 2;
+  v.lay.ring_k_offset += bb * ring;
+  v.lay.ring_v_offset += bb * ring;
+  v.d.batch = 1;
+  v.n = L->nseq[b];
+  v.nseq = &v.n;
+  v.ragged = false;
+  return v;
+}
+
+// Sequence b grew by T tokens: its count, the maximum, the ragged flag.
+static void advance_sequence(duo_layer* L, int32_t b, int64_t T) {
+  L->nseq[b] += T;
+  int64_t mx = L->nseq[0];
+  bool ragged = false;
+  for (int32_t i = 1; i < L->d.batch; ++i) {
+    if (L->nseq[i] != L->nseq[0]) ragged = true;
+    if (L->nseq[i] > mx) mx = L->nseq[i];
+  }
+  L->n = mx;
+  L->ragged = ragged;
+}
+
+static duo_status check_sequence(const duo_layer* L, int32_t b, int32_t T) {
+  if (!L || b < 0 || b >= L->d.batch || T < 1) return DUO_ERR_INVALID_ARG;
+  // a layer whose counts may differ passes them to the decode kernels
+  if (L->d.batch > kMaxRaggedBatch) return DUO_ERR_UNSUPPORTED;
+  if (L->Hr > 0 && L->nseq[b] + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
+  if (L->nseq[b] + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
+  return DUO_OK;
+}
+
+duo_status duo_append_kv_seq(duo_layer* L, int32_t b, const void* k, const void* v, int32_t T,
+                             hipStream_t stream) {
+  duo_status st = check_sequence(L, b, T);
+  if (st != DUO_OK) return st;
+  if ((st = check_act(k)) != DUO_OK || (st = check_act(v)) != DUO_OK) return st;
+  duo_layer view = sequence_view(L, b);
+  if (view.Hr > 0 && launch_append_cache(&view, k, v, T, stream) != hipSuccess)
+    return DUO_ERR_HIP;
+  if (view.Hs > 0 && launch_append_ring(&view, k, v, T, stream) != hipSuccess)
+    return DUO_ERR_HIP;
+  advance_sequence(L, b, T);
+  return DUO_OK;
+}
+
+duo_status duo_prefill_chunk_seq(duo_layer* L, int32_t b, const void* q, const void* k,
+                                 const void* v, int32_t T, void* out, hipStream_t stream) {
+  duo_status st = check_sequence(L, b, T);
+  if (st != DUO_OK) return st;
+  if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
+      (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
+    return st;
+  if (L->d.kv_dtype != DUO_BF16 || L->d.retrieval_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  duo_layer view = sequence_view(L, b);
+  if ((st = prefill_launch(&view, q, k, v, T, out, stream)) != DUO_OK) return st;
+  advance_sequence(L, b, T);
   return DUO_OK;
 }
 

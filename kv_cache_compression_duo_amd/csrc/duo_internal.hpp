@@ -11,7 +11,9 @@ struct duo_layer {
   char* rbuf;
   char* sbuf;
   char* ws;
-  int64_t n;      // tokens cached
+  int64_t n;      // tokens cached: the largest count over the batch's sequences
+  int64_t* nseq;  // tokens cached per sequence [batch] (owned)
+  bool ragged;    // the sequences' counts differ
   int G, Hr, Hs;  // group size, retrieval / streaming KV heads
   int max_split;  // split-K partial slots per retrieval (batch, KV head)
   int cus;        // compute units of the device the layer was attached on
@@ -22,6 +24,9 @@ namespace duo {
 // Workspace layout: [counters: B*Hr u32, padded to 256 B][m,l: B*Hr*G*max_split*2 f32]
 //                   [acc: B*Hr*G*max_split*D f32]
 constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
+// Layers whose sequences hold different token counts pass the counts to the
+// decode kernels in their arguments: at most this many sequences.
+constexpr int kMaxRaggedBatch = 64;
 // Rows of readable (never used) memory after a bf16/fp16 retrieval buffer: a
 // decode tile of 32 rows starting at any valid row stays inside the buffer.
 constexpr int kDecodePadRows = 32;

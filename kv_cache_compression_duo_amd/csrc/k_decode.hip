@@ -42,9 +42,13 @@ struct DecodeArgs {
   float* acc;             // [B][Hr][G][max_split][D]
   int Hq, Hkv, Hr, Hs, S, R, max_split;
   int64_t cap;
-  int n;                  // position of the new token
+  int n;                  // position of the new token (every sequence unless ragged)
   int n_split, split_tokens;
+  int ragged;             // sequences hold different counts (use nseq)
   float qscale;           // softmax scale * log2(e)
+  // per-sequence positions last: the fields every block reads stay on
+  // the first lines of the argument block
+  int nseq[kMaxRaggedBatch];  // position of the new token per sequence
 };
 
 constexpr int kDecodeWaves = 4;  // waves per block
@@ -64,6 +68,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const bool retrieval = (int)blockIdx.x >= a.Hs;
   const int rb = (int)blockIdx.x - a.Hs;
   const int kvh = retrieval ? rb / a.n_split : a.Hr + (int)blockIdx.x;
+  // this sequence's new-token position (sequences may hold different counts;
+  // the splits cover the longest, so a shorter one's last splits are empty)
+  int n = a.n;
+  if (a.ragged) n = a.nseq[b];  // only layers of at most kMaxRaggedBatch sequences
 
   // query fragments, pre-scaled into the log2 domain
   float qf[G][8];
@@ -83,14 +91,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     const int split = rb % a.n_split;
     const int r0 = split * a.split_tokens;
     int r1 = r0 + a.split_tokens;
-    if (r1 > a.n + 1) r1 = a.n + 1;
+    if (r1 > n + 1) r1 = n + 1;
     const int64_t hb = (int64_t)b * a.Hr + kvh;
     const uint16_t* kc = a.kc + hb * a.cap * D;
     const uint16_t* vc = a.vc + hb * a.cap * D;
-    const int n = a.n;
     // cache rows [r0, min(r1, n)); the split holding position n adds the
-    // new token from its input
-    const bool has_new = r1 == n + 1;
+    // new token from its input; splits past n are empty (m = -inf)
+    const bool has_new = r0 <= n && r1 == n + 1;
     QFrag<G> qfrag;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -144,8 +151,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     // Lambda mask allows for the new token
     const int hs = kvh - a.Hr;
     const int W = a.S + a.R;
-    const int nslots = a.n + 1 < W ? a.n + 1 : W;
-    const int slot_new = a.n < a.S ? a.n : a.S + (a.n - a.S) % a.R;
+    const int nslots = n + 1 < W ? n + 1 : W;
+    const int slot_new = n < a.S ? n : a.S + (n - a.S) % a.R;
     const int64_t hb = (int64_t)b * a.Hs + hs;
     const uint16_t* kr = a.kr + hb * W * D;
     const uint16_t* vr = a.vr + hb * W * D;
@@ -212,8 +219,10 @@ hipError_t launch_decode(const duo_layer* L, const void* q, const void* k_new,
   a.max_split = L->max_split;
   a.cap = d.retrieval_capacity;
   a.n = (int)L->n;
+  a.ragged = L->ragged ? 1 : 0;
+  for (int b = 0; b < d.batch && b < kMaxRaggedBatch; ++b) a.nseq[b] = (int)L->nseq[b];
   a.qscale = d.softmax_scale * kLog2e;
-  const int64_t rows = L->n + 1;
+  const int64_t rows = L->n + 1;  // the longest sequence
   const int B = d.batch;
   const int st = decode_split_tokens(L, rows, 1, L->cus * 4 / 5);
   const int ms = L->max_split;

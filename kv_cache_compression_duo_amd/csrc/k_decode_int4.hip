@@ -66,9 +66,14 @@ struct Int4DecodeArgs {
   float* acc;
   int Hq, Hkv, Hr, Hs, S, R, max_split;
   int64_t cap32;
-  int n;                   // position of the new token (quantised into the cache here)
+  int n;                   // position of the new token (quantised into the cache here),
+                           // every sequence unless ragged
   int n_split, split_tokens;
+  int ragged;             // sequences hold different counts (use nseq)
   float qscale;            // softmax scale * log2(e)
+  // per-sequence positions last: the fields every block reads stay on
+  // the first lines of the argument block
+  int nseq[kMaxRaggedBatch];  // position of the new token per sequence
 };
 
 // 8 nibbles of a word -> 8 16-bit lanes whose low byte is the code and high
@@ -188,6 +193,10 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   const bool retrieval = (int)blockIdx.x >= a.Hs;
   const int rb = (int)blockIdx.x - a.Hs;
   const int kvh = retrieval ? rb / a.n_split : a.Hr + (int)blockIdx.x;
+  // this sequence's new-token position (sequences may hold different counts;
+  // the splits cover the longest, so a shorter one's last splits are empty)
+  int n = a.n;
+  if (a.ragged) n = a.nseq[b];  // only layers of at most kMaxRaggedBatch sequences
 
   if (!retrieval) {
     // streaming head: identical to the bf16/fp16 decode path
@@ -205,8 +214,8 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
     const uint16_t* vnew = a.v_new + ((int64_t)b * a.Hkv + kvh) * D;
     const int hs = kvh - a.Hr;
     const int Wr = a.S + a.R;
-    const int nslots = a.n + 1 < Wr ? a.n + 1 : Wr;
-    const int slot_new = a.n < a.S ? a.n : a.S + (a.n - a.S) % a.R;
+    const int nslots = n + 1 < Wr ? n + 1 : Wr;
+    const int slot_new = n < a.S ? n : a.S + (n - a.S) % a.R;
     const int64_t hb = (int64_t)b * a.Hs + hs;
     const uint16_t* kr = a.kr + hb * Wr * D;
     const uint16_t* vr = a.vr + hb * Wr * D;
@@ -230,11 +239,11 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   // ---------------------------------------------------------------- retrieval
   const int split = rb % a.n_split;
   const int r0 = split * a.split_tokens;
-  const int r_end = r0 + a.split_tokens < a.n + 1 ? r0 + a.split_tokens : a.n + 1;
+  const int r_end = r0 + a.split_tokens < n + 1 ? r0 + a.split_tokens : n + 1;
   // the split holding position n also takes the new token, which it quantises
   // itself (below); its cache rows end at n
-  const bool has_new = r_end == a.n + 1;
-  const int r1 = has_new ? a.n : r_end;
+  const bool has_new = r0 <= n && r_end == n + 1;  // splits past n are empty
+  const int r1 = has_new ? n : r_end;
   const int64_t hb = (int64_t)b * a.Hr + kvh;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int hc = n16 / NG, gc = n16 % NG;  // this lane's (head, group) column
@@ -419,7 +428,6 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
     const uint16_t* src = (vside ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + kvh) * D + 8 * c;
     uint32_t codes, sz;
     encode_group_part<RingTag>(ld16(src), &codes, &sz);
-    const int n = a.n;
     if (act) {
       const int64_t w = ((hb * (a.cap32 / 32) + n / 32) * NG + c / 4) * 32 + n % 32;
       if (!vside) {
@@ -600,8 +608,10 @@ hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_n
   a.max_split = L->max_split;
   a.cap32 = cap32_of(d.retrieval_capacity);
   a.n = (int)L->n;
+  a.ragged = L->ragged ? 1 : 0;
+  for (int b = 0; b < d.batch && b < kMaxRaggedBatch; ++b) a.nseq[b] = (int)L->nseq[b];
   a.qscale = d.softmax_scale * kLog2e;
-  const int64_t rows = L->n + 1;
+  const int64_t rows = L->n + 1;  // the longest sequence
   const int B = d.batch;
   const int st = decode_split_tokens(L, rows, 32, L->cus);
   const int ms = L->max_split;

@@ -61,12 +61,15 @@ __device__ void merge_splits(MergeLds<NT>& s, const float* __restrict__ ml,
       float mx = m;
 #pragma unroll
       for (int u = 0; u < UN; ++u) mx = fmaxf(mx, mlv[u].x);
-      const float c = fast_exp2(m - mx);  // m = -inf on the first batch -> 0
+      // a split with no row (m = -inf: past a shorter sequence's end) has
+      // weight 0; guard -inf - -inf when every split so far is empty
+      const float c = m == -INFINITY ? 0.0f : fast_exp2(m - mx);
       l *= c;
       o *= c;
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const float w = sp0 + u * P < n_split ? fast_exp2(mlv[u].x - mx) : 0.0f;
+        const bool use = sp0 + u * P < n_split && mlv[u].x != -INFINITY;
+        const float w = use ? fast_exp2(mlv[u].x - mx) : 0.0f;
         l = fmaf(mlv[u].y, w, l);
         o = fmaf(aa[u], w, o);
       }

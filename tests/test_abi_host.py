@@ -211,6 +211,26 @@ def test_reorder_head_rows_matches_oracle_bit_for_bit():
     np.testing.assert_array_equal(dst, np.concatenate([src[8:12], src[0:4], src[4:8]]))
 
 
+def test_ragged_init_and_sequence_calls_validate_first():
+    L = _lib()
+    h = ctypes.c_void_p()
+    d = _desc(batch=3)  # capacity 1000
+    init = L.lib.duo_layer_init_ragged
+    by = ctypes.byref
+    assert init(by(h), by(d), 0x1000, 0x2000, 0x3000, None, None) == 1
+    assert init(by(h), by(d), 0x1000, 0x2000, 0x3000, (ctypes.c_int64 * 3)(10, -1, 7), None) == 1
+    assert init(by(h), by(d), 0x1000, 0x2000, 0x3000, (ctypes.c_int64 * 3)(10, 5, 1001),
+                None) == 4
+    assert init(by(h), by(d), 0x1008, 0x2000, 0x3000, (ctypes.c_int64 * 3)(10, 5, 7), None) == 3
+    d65 = _desc(batch=65)
+    counts = (ctypes.c_int64 * 65)(*([3] * 64 + [4]))
+    assert init(by(h), by(d65), 0x1000, 0x2000, 0x3000, counts, None) == 2
+    assert h.value is None
+    assert L.lib.duo_layer_sequence_tokens(None, 0) == -1
+    assert L.lib.duo_append_kv_seq(None, 0, 0x1000, 0x1000, 4, None) == 1
+    assert L.lib.duo_prefill_chunk_seq(None, 0, 0x1000, 0x1000, 0x1000, 4, 0x1000, None) == 1
+
+
 def test_status_strings():
     L = _lib()
     assert L.status_string(0) == "ok"
