@@ -16,8 +16,8 @@ Sources (cited by page and section):
     paperlayer.ai (sections 1-5, A.1-A.5).
   * scime atlas summary -- the same title, AI summary on atlas.scime.ai.
 
-Readings where the pages are silent or garbled are listed where they are used
-and collected in the design doc. Every function here is pinned by tests in
+Readings where the pages are silent or garbled are stated where they are
+used. Every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against brute force, a library routine, closed
 forms or the pages' invariants; the one exception is marked
 "parity unpinned" in its docstring (none at present).
