@@ -113,7 +113,9 @@ typedef struct duo_layer duo_layer; /* opaque host object */
 
 /* Sizes and offsets of the buffers a layer needs. Host-only; no HIP call.
  * Errors: DUO_ERR_INVALID_ARG for a null pointer or a bad descriptor,
- * DUO_ERR_UNSUPPORTED for an unsupported head_dim, group size or dtype. */
+ * DUO_ERR_UNSUPPORTED for an unsupported head_dim, group size or dtype or a
+ * batch above 65535, DUO_ERR_CAPACITY when a buffer of the layout would
+ * exceed 2^62 bytes. */
 duo_status duo_layer_layout(const duo_layer_desc* desc, duo_layout* layout);
 
 /* Attach a layer to caller-owned device buffers of at least the sizes

@@ -3,6 +3,7 @@
 // a failed call enqueues nothing and leaves the layer unchanged.
 #include <math.h>
 #include <algorithm>
+#include <initializer_list>
 #include <new>
 #include <vector>
 #include <stdlib.h>
@@ -30,13 +31,15 @@ int max_split_for(const duo_layer_desc& d) {
 // faster than 48). Streaming-head blocks read at most S + R rows, so four of
 // them are counted as one block. DUO_DECODE_SPLIT_TOKENS, if set to a
 // positive value, overrides the rule.
+static int split_tokens_override() {
+  const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
+  const int v = e ? atoi(e) : 0;
+  return v > 0 ? v : 0;
+}
+
 int decode_split_tokens(const duo_layer* L, int64_t rows, int tile, int blocks) {
-  static int env = -1;
-  if (env < 0) {
-    const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
-    env = e ? atoi(e) : 0;
-    if (env < 0) env = 0;
-  }
+  // read once; the initialisation of a local static is thread-safe
+  static const int env = split_tokens_override();
   int64_t st = env;
   if (st <= 0) {
     const int B = L->d.batch;
@@ -71,9 +74,21 @@ WsView ws_view(const duo_layer* L) {
   return v;
 }
 
+// true when the product of the factors stays at or below 2^62 bytes (no
+// buffer of a layer is larger; the bound also keeps every sum of such
+// products below 2^64)
+static bool size_ok(std::initializer_list<size_t> factors) {
+  size_t r = 1;
+  for (size_t x : factors)
+    if (__builtin_mul_overflow(r, x, &r) || r > ((size_t)1 << 62)) return false;
+  return true;
+}
+
 static duo_status check_desc(const duo_layer_desc* d) {
   if (!d) return DUO_ERR_INVALID_ARG;
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return DUO_ERR_INVALID_ARG;
+  // the batch index is a grid dimension of at most 65535 blocks
+  if (d->batch > 65535) return DUO_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads) return DUO_ERR_INVALID_ARG;
   int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return DUO_ERR_UNSUPPORTED;
@@ -88,6 +103,16 @@ static duo_status check_desc(const duo_layer_desc* d) {
   if (d->retrieval_dtype != d->kv_dtype && d->retrieval_dtype != DUO_INT4_G32)
     return DUO_ERR_UNSUPPORTED;
   if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.0f)) return DUO_ERR_INVALID_ARG;
+  // every buffer size of the layout must be representable
+  {
+    const size_t B = (size_t)d->batch, D = (size_t)d->head_dim;
+    const size_t cap = (size_t)cap32_of(d->retrieval_capacity) + kDecodePadRows;
+    const size_t G = (size_t)(d->n_q_heads / d->n_kv_heads);
+    if (!size_ok({B, (size_t)d->n_kv_heads, cap, D, 4}) ||
+        !size_ok({B, (size_t)d->n_kv_heads, (size_t)(d->sink + d->recent), D, 4}) ||
+        !size_ok({B, (size_t)d->n_kv_heads, G, (size_t)max_split_for(*d), D + 2, 4}))
+      return DUO_ERR_CAPACITY;
+  }
   // the 4-bit decode kernel maps (query head, channel group) pairs of a KV
   // head onto the 16 columns of one MFMA tile
   if (d->retrieval_dtype == DUO_INT4_G32 && G * (d->head_dim / 32) > 16) return DUO_ERR_UNSUPPORTED;
