@@ -500,9 +500,14 @@ duo_status duo_binarize_gates(const float* alpha, int32_t n, double sparsity, ui
     memset(mask, 0, (size_t)n);
     return DUO_OK;
   }
-  std::vector<float> sorted(alpha, alpha + n);
-  std::nth_element(sorted.begin(), sorted.begin() + n_stream, sorted.end());
-  const float tau = sorted[(size_t)n_stream];
+  float tau;
+  try {  // no exception (an allocation failure) may leave through the C ABI
+    std::vector<float> sorted(alpha, alpha + n);
+    std::nth_element(sorted.begin(), sorted.begin() + n_stream, sorted.end());
+    tau = sorted[(size_t)n_stream];
+  } catch (...) {
+    return DUO_ERR_INVALID_ARG;
+  }
   for (int32_t i = 0; i < n; ++i) mask[i] = alpha[i] >= tau ? 1 : 0;
   return DUO_OK;
 }
@@ -518,10 +523,14 @@ duo_status duo_reorder_head_rows(const void* in, void* out, const int32_t* perm,
   const char* src = static_cast<const char*>(in);
   char* dst = static_cast<char*>(out);
   if (src < dst + total && dst < src + total) return DUO_ERR_LAYOUT;  // overlapping buffers
-  std::vector<uint8_t> seen((size_t)n_heads, 0);
-  for (int32_t i = 0; i < n_heads; ++i) {
-    if (perm[i] < 0 || perm[i] >= n_heads || seen[(size_t)perm[i]]) return DUO_ERR_INVALID_ARG;
-    seen[(size_t)perm[i]] = 1;
+  try {  // as above: allocation failures become a status
+    std::vector<uint8_t> seen((size_t)n_heads, 0);
+    for (int32_t i = 0; i < n_heads; ++i) {
+      if (perm[i] < 0 || perm[i] >= n_heads || seen[(size_t)perm[i]]) return DUO_ERR_INVALID_ARG;
+      seen[(size_t)perm[i]] = 1;
+    }
+  } catch (...) {
+    return DUO_ERR_INVALID_ARG;
   }
   for (int32_t i = 0; i < n_heads; ++i)
     memcpy(dst + (size_t)i * block, src + (size_t)perm[i] * block, block);
