@@ -26,11 +26,19 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
-def _check_act(t: torch.Tensor, name: str, shape, dtype):
+def _gpu(device) -> torch.device:
+    """The device with its index resolved (the library has no host path)."""
+    dev = torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError(f"device {dev} is not a GPU")
+    return dev if dev.index is not None else torch.device("cuda", torch.cuda.current_device())
+
+
+def _check_act(t: torch.Tensor, name: str, shape, dtype, device: torch.device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
@@ -58,7 +66,7 @@ class DuoLayer:
                               sink=sink, recent=recent, capacity=capacity, kv_dtype=kv_dtype,
                               retrieval_dtype=retrieval_dtype, softmax_scale=softmax_scale)
         self.layout = layout(self.desc)
-        self.device = torch.device(device)
+        self.device = _gpu(device)
         self.B, self.Hq, self.Hkv, self.D = batch, n_q_heads, n_kv_heads, head_dim
         self.Hr, self.Hs = n_retrieval_kv_heads, n_kv_heads - n_retrieval_kv_heads
         self.G = n_q_heads // n_kv_heads
@@ -74,13 +82,15 @@ class DuoLayer:
             if len(n_tokens_existing) != batch:
                 raise ValueError("n_tokens_existing needs one count per sequence")
             counts = (c_int64 * batch)(*[int(x) for x in n_tokens_existing])
-            check(lib.duo_layer_init_ragged(byref(h), byref(self.desc), _ptr(self.rbuf),
-                                            _ptr(self.sbuf), _ptr(self.ws), counts,
-                                            _stream_ptr(self.device)), "duo_layer_init_ragged")
+            with torch.cuda.device(self.device):
+                check(lib.duo_layer_init_ragged(byref(h), byref(self.desc), _ptr(self.rbuf),
+                                                _ptr(self.sbuf), _ptr(self.ws), counts,
+                                                _stream_ptr(self.device)), "duo_layer_init_ragged")
         else:
-            check(lib.duo_layer_init(byref(h), byref(self.desc), _ptr(self.rbuf), _ptr(self.sbuf),
-                                     _ptr(self.ws), int(n_tokens_existing),
-                                     _stream_ptr(self.device)), "duo_layer_init")
+            with torch.cuda.device(self.device):
+                check(lib.duo_layer_init(byref(h), byref(self.desc), _ptr(self.rbuf), _ptr(self.sbuf),
+                                         _ptr(self.ws), int(n_tokens_existing),
+                                         _stream_ptr(self.device)), "duo_layer_init")
         self._h = h
 
     def close(self):
@@ -106,57 +116,62 @@ class DuoLayer:
     def append_kv(self, k: torch.Tensor, v: torch.Tensor):
         T = k.shape[1]
         kvt = _TORCH[self.kv_dtype]
-        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt)
-        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt)
-        check(lib.duo_append_kv(self._h, _ptr(k), _ptr(v), T, _stream_ptr(self.device)),
-              "duo_append_kv")
+        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt, self.device)
+        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt, self.device)
+        with torch.cuda.device(self.device):
+            check(lib.duo_append_kv(self._h, _ptr(k), _ptr(v), T, _stream_ptr(self.device)),
+                  "duo_append_kv")
 
     def prefill_chunk(self, q, k, v, out=None):
         T = q.shape[1]
         kvt = _TORCH[self.kv_dtype]
-        _check_act(q, "q", (self.B, T, self.Hq, self.D), torch.bfloat16)
-        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt)
-        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt)
+        _check_act(q, "q", (self.B, T, self.Hq, self.D), torch.bfloat16, self.device)
+        _check_act(k, "k", (self.B, T, self.Hkv, self.D), kvt, self.device)
+        _check_act(v, "v", (self.B, T, self.Hkv, self.D), kvt, self.device)
         if out is None:
             out = torch.empty_like(q)
-        _check_act(out, "out", (self.B, T, self.Hq, self.D), torch.bfloat16)
-        check(lib.duo_prefill_chunk(self._h, _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
-                                    _stream_ptr(self.device)), "duo_prefill_chunk")
+        _check_act(out, "out", (self.B, T, self.Hq, self.D), torch.bfloat16, self.device)
+        with torch.cuda.device(self.device):
+            check(lib.duo_prefill_chunk(self._h, _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
+                                        _stream_ptr(self.device)), "duo_prefill_chunk")
         return out
 
     def append_kv_seq(self, b: int, k: torch.Tensor, v: torch.Tensor):
         """Append to sequence b alone: k/v [1, T, Hkv, D]."""
         T = k.shape[1]
         kvt = _TORCH[self.kv_dtype]
-        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt)
-        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt)
-        check(lib.duo_append_kv_seq(self._h, int(b), _ptr(k), _ptr(v), T,
-                                    _stream_ptr(self.device)), "duo_append_kv_seq")
+        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt, self.device)
+        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt, self.device)
+        with torch.cuda.device(self.device):
+            check(lib.duo_append_kv_seq(self._h, int(b), _ptr(k), _ptr(v), T,
+                                        _stream_ptr(self.device)), "duo_append_kv_seq")
 
     def prefill_chunk_seq(self, b: int, q, k, v, out=None):
         """Prefill a chunk of sequence b alone: q [1, T, Hq, D], k/v [1, T, Hkv, D]."""
         T = q.shape[1]
         kvt = _TORCH[self.kv_dtype]
-        _check_act(q, "q", (1, T, self.Hq, self.D), torch.bfloat16)
-        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt)
-        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt)
+        _check_act(q, "q", (1, T, self.Hq, self.D), torch.bfloat16, self.device)
+        _check_act(k, "k", (1, T, self.Hkv, self.D), kvt, self.device)
+        _check_act(v, "v", (1, T, self.Hkv, self.D), kvt, self.device)
         if out is None:
             out = torch.empty_like(q)
-        _check_act(out, "out", (1, T, self.Hq, self.D), torch.bfloat16)
-        check(lib.duo_prefill_chunk_seq(self._h, int(b), _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
-                                        _stream_ptr(self.device)), "duo_prefill_chunk_seq")
+        _check_act(out, "out", (1, T, self.Hq, self.D), torch.bfloat16, self.device)
+        with torch.cuda.device(self.device):
+            check(lib.duo_prefill_chunk_seq(self._h, int(b), _ptr(q), _ptr(k), _ptr(v), T, _ptr(out),
+                                            _stream_ptr(self.device)), "duo_prefill_chunk_seq")
         return out
 
     def decode(self, q, k, v, out=None):
         kvt = _TORCH[self.kv_dtype]
-        _check_act(q, "q", (self.B, 1, self.Hq, self.D), torch.bfloat16)
-        _check_act(k, "k", (self.B, 1, self.Hkv, self.D), kvt)
-        _check_act(v, "v", (self.B, 1, self.Hkv, self.D), kvt)
+        _check_act(q, "q", (self.B, 1, self.Hq, self.D), torch.bfloat16, self.device)
+        _check_act(k, "k", (self.B, 1, self.Hkv, self.D), kvt, self.device)
+        _check_act(v, "v", (self.B, 1, self.Hkv, self.D), kvt, self.device)
         if out is None:
             out = torch.empty_like(q)
-        _check_act(out, "out", (self.B, 1, self.Hq, self.D), torch.bfloat16)
-        check(lib.duo_decode(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                             _stream_ptr(self.device)), "duo_decode")
+        _check_act(out, "out", (self.B, 1, self.Hq, self.D), torch.bfloat16, self.device)
+        with torch.cuda.device(self.device):
+            check(lib.duo_decode(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _stream_ptr(self.device)), "duo_decode")
         return out
 
     # -- views of the caller-owned caches (documented layout) -------------------
@@ -207,20 +222,22 @@ def mixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     """out_h = alpha[h // G] * full_h + (1 - alpha[h // G]) * streaming_h.
     q [B,T,Hq,D] bf16, k/v [B,T,Hkv,D] bf16, alpha [Hkv] fp32 (device).
     lambda_block = 64 takes the streaming part under the block-sparse mask."""
+    dev = _gpu(q.device)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16)
-    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16)
-    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16)
-    _check_act(alpha, "alpha", (Hkv,), torch.float32)
+    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16, dev)
+    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(alpha, "alpha", (Hkv,), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
-    _check_act(out, "out", (B, T, Hq, D), torch.bfloat16)
+    _check_act(out, "out", (B, T, Hq, D), torch.bfloat16, dev)
     desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
                      sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
-    check(lib.duo_mixed_forward_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), T,
-                                      int(lambda_block), _ptr(out), _stream_ptr(q.device)),
-          "duo_mixed_forward_block")
+    with torch.cuda.device(dev):
+        check(lib.duo_mixed_forward_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), T,
+                                          int(lambda_block), _ptr(out), _stream_ptr(dev)),
+              "duo_mixed_forward_block")
     return out
 
 
@@ -233,26 +250,29 @@ def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: to
     query heads of KV head kv and channels, + l1_weight * sign(alpha[kv]).
     dout [B,T,Hq,D] bf16; returns grad [Hkv] fp32 (device). The workspace
     (uint8 device tensor) is allocated here unless given."""
+    dev = _gpu(q.device)
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16)
-    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16)
-    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16)
-    _check_act(dout, "dout", (B, T, Hq, D), torch.bfloat16)
-    _check_act(alpha, "alpha", (Hkv,), torch.float32)
+    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16, dev)
+    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(dout, "dout", (B, T, Hq, D), torch.bfloat16, dev)
+    _check_act(alpha, "alpha", (Hkv,), torch.float32, dev)
     if grad is None:
         grad = torch.empty(Hkv, dtype=torch.float32, device=q.device)
-    _check_act(grad, "grad", (Hkv,), torch.float32)
+    _check_act(grad, "grad", (Hkv,), torch.float32, dev)
     desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
                      sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
     need = int(lib.duo_mixed_alpha_grad_workspace(byref(desc), T))
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    check(lib.duo_mixed_alpha_grad_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-                                         _ptr(alpha), float(l1_weight), T, int(lambda_block),
-                                         _ptr(grad), _ptr(workspace), workspace.numel(),
-                                         _stream_ptr(q.device)),
-          "duo_mixed_alpha_grad_block")
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check_act(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    with torch.cuda.device(dev):
+        check(lib.duo_mixed_alpha_grad_block(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                             _ptr(alpha), float(l1_weight), T, int(lambda_block),
+                                             _ptr(grad), _ptr(workspace), workspace.numel(),
+                                             _stream_ptr(dev)),
+              "duo_mixed_alpha_grad_block")
     return grad
 
 

@@ -259,3 +259,19 @@ def test_ring_slot_matches_oracle():
             assert ring_slot(p, S, R) == oracle.ring_slot(p, S, R)
     assert ring_slot(-1, 16, 64) == -1
     assert ring_slot(3, 16, 0) == -1
+
+
+def test_binding_has_no_host_path():
+    """The Python calls refuse host tensors and a host device before any
+    library call: there is no CPU fallback."""
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    a = torch.zeros(2)
+    with pytest.raises(ValueError, match="not a GPU"):
+        duo.mixed_forward(q, q, q, a, softmax_scale=0.125)
+    with pytest.raises(ValueError, match="not a GPU"):
+        duo.mixed_alpha_grad(q, q, q, q, a, softmax_scale=0.125)
+    with pytest.raises(ValueError, match="not a GPU"):
+        duo.DuoLayer(n_q_heads=2, n_kv_heads=2, head_dim=64, n_retrieval_kv_heads=1,
+                     capacity=16, softmax_scale=0.125, device="cpu")
