@@ -35,6 +35,7 @@ def _forward(q, k, v, alpha, scale, S, R):
     (700, 4, 4, 64, 100, 130),   # two sink blocks, three local blocks
     (260, 8, 2, 128, 0, 64),     # no sinks
     (129, 16, 2, 128, 64, 65),   # block-aligned sinks, two local blocks
+    (300, 16, 2, 64, 16, 64),    # G=8, head_dim 64
 ])
 def test_block_mixed_forward_matches_oracle(T, Hq, Hkv, D, S, R):
     scale = D ** -0.5
@@ -76,6 +77,7 @@ def test_block_mixed_full_length_sampled():
 @pytest.mark.parametrize("T,Hq,Hkv,D,S,R", [
     (333, 8, 4, 128, 16, 64),
     (400, 4, 2, 64, 100, 130),
+    (200, 16, 2, 64, 16, 64),    # G=8, head_dim 64
 ])
 def test_block_alpha_grad_matches_oracle(T, Hq, Hkv, D, S, R):
     import kv_cache_compression_duo_amd as duo

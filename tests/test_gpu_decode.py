@@ -144,6 +144,20 @@ def test_decode_all_streaming_or_all_retrieval(heads):
     _run_decode_case(inp, context=700, steps=3, label=f"hr{len(heads)}")
 
 
+@pytest.mark.parametrize("G,D,kv_dtype", [(1, 64, "fp16"), (2, 64, "bf16"), (2, 128, "fp16"),
+                                          (4, 64, "bf16"), (4, 128, "bf16"), (8, 64, "fp16")])
+def test_decode_group_sizes(G, D, kv_dtype):
+    """Each supported group size with both head dims and both 16-bit cache
+    dtypes, over a context spanning several split-K ranges and a ragged tail."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["llama3_8b_prefill_64k"], n_q_heads=3 * G, n_kv_heads=3,
+                            head_dim=D, fixed_retrieval=(0, 2), softmax_scale=D ** -0.5,
+                            kv_dtype=kv_dtype, ring_dtype=kv_dtype)
+    say(f"case: decode G={G} D={D} {kv_dtype}, context 1300 + 3 decode")
+    inp = make_inputs(w, tokens=1300, steps=3, seed=4100 + 10 * G + D)
+    _run_decode_case(inp, context=1300, steps=3, kv_dtype=kv_dtype, label=f"G{G}D{D}{kv_dtype}")
+
+
 def test_decode_batch2_and_group8():
     import dataclasses
     w = dataclasses.replace(WORKLOADS["llama3_8b_int4_decode_1m"], n_q_heads=16, n_kv_heads=2,
