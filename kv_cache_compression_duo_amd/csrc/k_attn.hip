@@ -445,18 +445,40 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       // masked in place: unmasked tiles use the product registers as they are
       // (a separate masked copy cost 32 moves per tile on the unmasked path)
       if (lam_phase || diag) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int jp = p0 + 32 * kb + 8 * (j >> 2) + 4 * h2 + (j & 3);
-            // bitwise operators: a select per element, no per-lane branches
-            const bool causal = jp <= i_q;
-            const bool lam =
-                causal & (lblk ? (((jp >> 6) < sbk) | (((i_q >> 6) - (jp >> 6)) < rbk))
-                               : ((jp < a.S) | (i_q - jp < a.R)));
-            st[kb][j] = (lam_phase ? lam : causal) ? st[kb][j] : -INFINITY;
+        // Element j of the lane's scores is key base + c_j, with c_j a
+        // compile-time offset. One loop per mode (a tile-uniform branch
+        // between two loops made the compiler copy the scores at the join
+        // on every tile). Bitwise operators: a select per element, no
+        // per-lane branches.
+        const int base = p0 + 4 * h2;
+        if constexpr (MODE == MODE_RETRIEVAL || lblk) {
+          // causal: c_j <= dq; under the block mask a 64-key tile is one
+          // block, visible to a query or not as a whole
+          int dq = i_q - base;
+          if constexpr (lblk) {
+            const bool vis = ((p0 >> 6) < sbk) | (((i_q >> 6) - (p0 >> 6)) < rbk);
+            dq = (lam_phase & !vis) ? -1 : dq;
           }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
+              st[kb][j] = c <= dq ? st[kb][j] : -INFINITY;
+            }
+        } else {
+          // token-level Lambda; outside the Lambda phase every key passes
+          // the sink test, leaving the causal one
+          const int s_lim = lam_phase ? a.S : 0x7fffffff;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int jp = base + 32 * kb + 8 * (j >> 2) + (j & 3);
+              const bool ok = (jp <= i_q) & ((jp < s_lim) | (i_q - jp < a.R));
+              st[kb][j] = ok ? st[kb][j] : -INFINITY;
+            }
+        }
       }
       bf16x8 pb[4];
       softmax_update(st, m_f, l_f, o_f, pb);
