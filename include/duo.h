@@ -129,9 +129,9 @@ duo_status duo_layer_init(duo_layer** out, const duo_layer_desc* desc, void* ret
 
 /* As duo_layer_init, for a batch whose sequences already hold different
  * token counts: n_tokens_existing[batch] (each within the capacity). Such a
- * ragged layer (batch <= 64; larger ragged batches return
- * DUO_ERR_UNSUPPORTED) decodes every sequence at its own position and grows
- * its sequences one at a time with duo_append_kv_seq / duo_prefill_chunk_seq
+ * ragged layer decodes every sequence at its own position (one launch per 64
+ * sequences) and grows its sequences one at a time with
+ * duo_append_kv_seq / duo_prefill_chunk_seq
  * (serving: sequences admitted at different times; paperlayer summary of
  * arXiv 2410.10819v1, section 4, and xllm-io review, section 三 推理流程). */
 duo_status duo_layer_init_ragged(duo_layer** out, const duo_layer_desc* desc, void* retrieval_buf,

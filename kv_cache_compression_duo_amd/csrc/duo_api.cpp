@@ -187,7 +187,6 @@ static duo_status layer_init(duo_layer** out, const duo_layer_desc* d, void* ret
     if (b > 0 && nb != n_max) ragged = true;
     if (b == 0 || nb > n_max) n_max = nb;
   }
-  if (ragged && d->batch > kMaxRaggedBatch) return DUO_ERR_UNSUPPORTED;
   if (lay.retrieval_bytes && !retrieval_buf) return DUO_ERR_INVALID_ARG;
   if (lay.streaming_bytes && !streaming_buf) return DUO_ERR_INVALID_ARG;
   if (!workspace) return DUO_ERR_INVALID_ARG;
@@ -295,10 +294,13 @@ duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const v
   if (L->ragged) return DUO_ERR_UNSUPPORTED;  // per sequence: duo_prefill_chunk_seq
   if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
-  return prefill_launch(L, q, k, v, T, out, stream);
+  if ((st = prefill_launch(L, q, k, v, T, out, stream)) != DUO_OK) return st;
+  advance_all(L, T);
+  return DUO_OK;
 }
 
-// The batch-wide prefill of a (view of a) layer, after validation.
+// The batch-wide prefill of a (view of a) layer, after validation; leaves the
+// token counts to the caller (a view shares its parent's count array).
 static duo_status prefill_launch(duo_layer* L, const void* q, const void* k, const void* v,
                                  int32_t T, void* out, hipStream_t stream) {
   // Retrieval heads: append the chunk, then attend causally over the cache.
@@ -312,9 +314,10 @@ static duo_status prefill_launch(duo_layer* L, const void* q, const void* k, con
     if (launch_prefill_streaming(L, q, k, v, T, out, stream) != hipSuccess) return DUO_ERR_HIP;
     if (launch_append_ring(L, k, v, T, stream) != hipSuccess) return DUO_ERR_HIP;
   }
-  advance_all(L, T);
-  return DUO_OK;
+  return DUO_OK;  // the caller advances the token counts
 }
+
+static duo_layer batch_view(const duo_layer* L, int32_t b0, int32_t nb);
 
 duo_status duo_decode(duo_layer* L, const void* q, const void* k_new, const void* v_new,
                       void* out, hipStream_t stream) {
@@ -325,23 +328,43 @@ duo_status duo_decode(duo_layer* L, const void* q, const void* k_new, const void
     return st;
   if (L->Hr > 0 && L->n + 1 > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->n + 1 > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
-  hipError_t e;
-  if (L->d.retrieval_dtype == DUO_INT4_G32 && L->Hr > 0)
-    e = launch_decode_int4(L, q, k_new, v_new, out, stream);
-  else
-    e = launch_decode(L, q, k_new, v_new, out, stream);
+  auto launch = [&](const duo_layer* V, size_t b0) {
+    const size_t qrow = (size_t)V->d.n_q_heads * V->d.head_dim * 2;
+    const size_t kvrow = (size_t)V->d.n_kv_heads * V->d.head_dim * 2;
+    const char* qb = static_cast<const char*>(q) + b0 * qrow;
+    const char* kb = static_cast<const char*>(k_new) + b0 * kvrow;
+    const char* vb = static_cast<const char*>(v_new) + b0 * kvrow;
+    char* ob = static_cast<char*>(out) + b0 * qrow;
+    return V->d.retrieval_dtype == DUO_INT4_G32 && V->Hr > 0
+               ? launch_decode_int4(V, qb, kb, vb, ob, stream)
+               : launch_decode(V, qb, kb, vb, ob, stream);
+  };
+  hipError_t e = hipSuccess;
+  if (L->ragged && L->d.batch > kMaxRaggedBatch) {
+    // the kernels take ragged positions in their arguments: decode the batch
+    // in slices of at most kMaxRaggedBatch sequences, one launch each
+    for (int32_t b0 = 0; b0 < L->d.batch && e == hipSuccess; b0 += kMaxRaggedBatch) {
+      const duo_layer view = batch_view(L, b0, std::min(kMaxRaggedBatch, L->d.batch - b0));
+      e = launch(&view, (size_t)b0);
+    }
+  } else {
+    e = launch(L, 0);
+  }
   if (e != hipSuccess) return DUO_ERR_HIP;
   advance_all(L, 1);
   return DUO_OK;
 }
 
-// A batch-1 view of sequence b of a layer: the same buffers at that
-// sequence's offsets (every array is laid out batch-major) and its count.
-static duo_layer sequence_view(const duo_layer* L, int32_t b) {
+// A view of sequences [b0, b0 + nb) of a layer: the same buffers at those
+// sequences' offsets (every array is laid out batch-major), their counts,
+// and the workspace from its start (calls on one layer are ordered on the
+// stream and every decode launch leaves its arrival counters at zero, so
+// consecutive launches of views may share it).
+static duo_layer batch_view(const duo_layer* L, int32_t b0, int32_t nb) {
   duo_layer v = *L;
   const duo_layer_desc& d = L->d;
   const size_t D = (size_t)d.head_dim, Hr = (size_t)L->Hr, Hs = (size_t)L->Hs;
-  const size_t W = (size_t)(d.sink + d.recent), bb = (size_t)b;
+  const size_t W = (size_t)(d.sink + d.recent), bb = (size_t)b0;
   if (d.retrieval_dtype == DUO_INT4_G32) {
     const size_t cap32 = (size_t)cap32_of(d.retrieval_capacity);
     const size_t codes = Hr * cap32 * (D / 2), sz = Hr * cap32 * (D / 32) * 4;
@@ -357,12 +380,18 @@ static duo_layer sequence_view(const duo_layer* L, int32_t b) {
   const size_t ring = Hs * W * D * 2;
   v.lay.ring_k_offset += bb * ring;
   v.lay.ring_v_offset += bb * ring;
-  v.d.batch = 1;
-  v.n = L->nseq[b];
-  v.nseq = &v.n;
+  v.d.batch = nb;
+  v.nseq = L->nseq + b0;
+  v.n = v.nseq[0];
   v.ragged = false;
+  for (int32_t i = 1; i < nb; ++i) {
+    if (v.nseq[i] != v.nseq[0]) v.ragged = true;
+    if (v.nseq[i] > v.n) v.n = v.nseq[i];
+  }
   return v;
 }
+
+static duo_layer sequence_view(const duo_layer* L, int32_t b) { return batch_view(L, b, 1); }
 
 // Sequence b grew by T tokens: its count, the maximum, the ragged flag.
 static void advance_sequence(duo_layer* L, int32_t b, int64_t T) {
@@ -379,8 +408,6 @@ static void advance_sequence(duo_layer* L, int32_t b, int64_t T) {
 
 static duo_status check_sequence(const duo_layer* L, int32_t b, int32_t T) {
   if (!L || b < 0 || b >= L->d.batch || T < 1) return DUO_ERR_INVALID_ARG;
-  // a layer whose counts may differ passes them to the decode kernels
-  if (L->d.batch > kMaxRaggedBatch) return DUO_ERR_UNSUPPORTED;
   if (L->Hr > 0 && L->nseq[b] + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->nseq[b] + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
   return DUO_OK;

@@ -609,6 +609,8 @@ hipError_t launch_decode_int4(const duo_layer* L, const void* q, const void* k_n
   a.cap32 = cap32_of(d.retrieval_capacity);
   a.n = (int)L->n;
   a.ragged = L->ragged ? 1 : 0;
+  // ragged positions travel in the arguments: larger batches come in slices
+  if (L->ragged && d.batch > kMaxRaggedBatch) return hipErrorInvalidValue;
   for (int b = 0; b < d.batch && b < kMaxRaggedBatch; ++b) a.nseq[b] = (int)L->nseq[b];
   a.qscale = d.softmax_scale * kLog2e;
   const int64_t rows = L->n + 1;  // the longest sequence

@@ -227,9 +227,6 @@ def test_ragged_init_and_sequence_calls_validate_first():
     assert init(by(h), by(d), 0x1000, 0x2000, 0x3000, (ctypes.c_int64 * 3)(10, 5, 1001),
                 None) == 4
     assert init(by(h), by(d), 0x1008, 0x2000, 0x3000, (ctypes.c_int64 * 3)(10, 5, 7), None) == 3
-    d65 = _desc(batch=65)
-    counts = (ctypes.c_int64 * 65)(*([3] * 64 + [4]))
-    assert init(by(h), by(d65), 0x1000, 0x2000, 0x3000, counts, None) == 2
     assert h.value is None
     assert L.lib.duo_layer_sequence_tokens(None, 0) == -1
     assert L.lib.duo_append_kv_seq(None, 0, 0x1000, 0x1000, 4, None) == 1

@@ -73,6 +73,28 @@ def test_ragged_decode(kv_dtype, contexts):
     assert [lay.sequence_tokens(b) for b in range(B)] == [c + steps for c in contexts]
 
 
+@pytest.mark.parametrize("retrieval_dtype", [None, "int4"])
+def test_ragged_decode_more_sequences_than_one_launch_takes(retrieval_dtype):
+    """70 sequences of different lengths: the decode runs in slices of 64
+    sequences, one launch each, sharing the workspace."""
+    int4 = retrieval_dtype == "int4"
+    base = WORKLOADS["llama3_8b_int4_decode_1m" if int4 else "mha8_d64_seq1024"]
+    w = dataclasses.replace(base, n_q_heads=4, n_kv_heads=2, fixed_retrieval=(1,))
+    g = np.random.default_rng(26000)
+    contexts = tuple(int(x) for x in g.integers(1, 200, size=70))
+    steps = 2
+    kv = "fp16" if int4 else "bf16"
+    say(f"case: ragged decode of 70 sequences ({retrieval_dtype or kv} retrieval cache)")
+    inps, lay, orcs, r, rq = _setup(w, 70, contexts, steps, 26000, kv_dtype=kv,
+                                    retrieval_dtype=retrieval_dtype, int4=int4)
+    dtype = torch.float16 if int4 else torch.bfloat16
+    for b, (x, o) in enumerate(zip(inps, orcs)):
+        lay.append_kv_seq(b, r.kv(to_dev(x.k, dtype))[None], r.kv(to_dev(x.v, dtype))[None])
+        o.append(x.k, x.v)
+    _decode(lay, r, inps, orcs, steps, dtype, rq, f"ragged70-{retrieval_dtype or kv}")
+    assert [lay.sequence_tokens(b) for b in range(70)] == [c + steps for c in contexts]
+
+
 def test_ragged_int4_decode():
     w = dataclasses.replace(WORKLOADS["llama3_8b_int4_decode_1m"], fixed_retrieval=(0, 3, 5, 6))
     contexts, steps = (700, 45), 3
