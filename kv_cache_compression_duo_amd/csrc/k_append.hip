@@ -17,20 +17,18 @@ namespace duo {
 
 // ---- verbatim retrieval rows -------------------------------------------------
 // One thread per 16-byte chunk: k/v [B][T][Hkv][D] -> cache [B][Hr][cap][D].
+// A block covers 256 / chunks consecutive tokens of one (sequence, head);
+// grid (token groups, Hr, B), chunks a power of two: no index division.
 __global__ void append_rows_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
-                                   u32x4* __restrict__ kc, u32x4* __restrict__ vc, int B, int T,
-                                   int Hkv, int Hr, int chunks, int64_t cap, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t total = (int64_t)B * T * Hr * chunks;
-  if (i >= total) return;
-  int c = (int)(i % chunks);
-  int64_t r = i / chunks;
-  int h = (int)(r % Hr);
-  r /= Hr;
-  int t = (int)(r % T);
-  int b = (int)(r / T);
-  int64_t src = (((int64_t)b * T + t) * Hkv + h) * chunks + c;
-  int64_t dst = (((int64_t)b * Hr + h) * cap + n + t) * chunks + c;
+                                   u32x4* __restrict__ kc, u32x4* __restrict__ vc, int T,
+                                   int Hkv, int Hr, int lchunks, int64_t cap, int64_t n) {
+  const int chunks = 1 << lchunks;
+  const int c = (int)threadIdx.x & (chunks - 1);
+  const int t = (int)blockIdx.x * ((int)blockDim.x >> lchunks) + ((int)threadIdx.x >> lchunks);
+  if (t >= T) return;
+  const int h = (int)blockIdx.y, b = (int)blockIdx.z;
+  const int64_t src = (((int64_t)b * T + t) * Hkv + h) * chunks + c;
+  const int64_t dst = (((int64_t)b * Hr + h) * cap + n + t) * chunks + c;
   kc[dst] = k[src];
   vc[dst] = v[src];
 }
@@ -155,7 +153,6 @@ hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v,
   int chunks = d.head_dim / 8;
   int64_t total = (int64_t)d.batch * T * L->Hr * chunks;
   if (total == 0) return hipSuccess;
-  unsigned grid = blocks_for(total, 256);
   if (d.retrieval_dtype == DUO_INT4_G32) {
     const int64_t cap32 = cap32_of(d.retrieval_capacity);
     const int64_t blk0 = L->n / 32, blk1 = (L->n + T - 1) / 32;
@@ -175,11 +172,16 @@ hipError_t launch_append_cache(const duo_layer* L, const void* k, const void* v,
           static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), kq, vq, ks, vs, d.batch, T,
           d.n_kv_heads, L->Hr, chunks, cap32, L->n, blk0, nblk);
   } else {
-    append_rows_kernel<<<grid, 256, 0, s>>>(
+    // grid dimensions y and z hold at most 65535 blocks
+    if (L->Hr > 65535 || d.batch > 65535) return hipErrorInvalidValue;
+    const int lchunks = chunks == 16 ? 4 : 3;  // head_dim 128 or 64
+    const int per_block = 256 >> lchunks;
+    const dim3 g3((unsigned)((T + per_block - 1) / per_block), (unsigned)L->Hr, (unsigned)d.batch);
+    append_rows_kernel<<<g3, 256, 0, s>>>(
         static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
         reinterpret_cast<u32x4*>(L->rbuf + L->lay.k_offset),
-        reinterpret_cast<u32x4*>(L->rbuf + L->lay.v_offset), d.batch, T, d.n_kv_heads, L->Hr,
-        chunks, d.retrieval_capacity, L->n);
+        reinterpret_cast<u32x4*>(L->rbuf + L->lay.v_offset), T, d.n_kv_heads, L->Hr, lchunks,
+        d.retrieval_capacity, L->n);
   }
   return hipGetLastError();
 }
