@@ -16,13 +16,17 @@ struct duo_layer {
   bool ragged;    // the sequences' counts differ
   int G, Hr, Hs;  // group size, retrieval / streaming KV heads
   int max_split;  // split-K partial slots per retrieval (batch, KV head)
+  int ws_batch;   // batch the workspace is laid out for: the attached layer's,
+                  // kept by views of some of its sequences
   int cus;        // compute units of the device the layer was attached on
 };
 
 namespace duo {
 
 // Workspace layout: [counters: B*Hr u32, padded to 256 B][m,l: B*Hr*G*max_split*2 f32]
-//                   [acc: B*Hr*G*max_split*D f32]
+//                   [acc: B*Hr*G*max_split*D f32], B the batch of the layer the
+// workspace was attached with (a view of fewer sequences keeps that layout and
+// uses the leading entries of each region).
 constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
 // Layers whose sequences hold different token counts pass the counts to the
 // decode kernels in their arguments: at most this many sequences.

@@ -43,8 +43,8 @@ def _setup(w, B, contexts, steps, seed, kv_dtype="bf16", retrieval_dtype=None, i
     return inps, lay, orcs, r, rq
 
 
-def _decode(lay, r, inps, orcs, steps, dtype, rq, label):
-    for s in range(steps):
+def _decode(lay, r, inps, orcs, steps, dtype, rq, label, first=0):
+    for s in range(first, first + steps):
         q = torch.stack([r.q(to_dev(x.q_steps[s]))[None] for x in inps]).contiguous()
         k = torch.stack([r.kv(to_dev(x.k_steps[s], dtype))[None] for x in inps]).contiguous()
         v = torch.stack([r.kv(to_dev(x.v_steps[s], dtype))[None] for x in inps]).contiguous()
@@ -151,3 +151,44 @@ def test_batch_calls_refuse_ragged_and_resume_when_equal():
         o.append(x.k, x.v)
     assert lay.n_tokens == 40 and lay.sequence_tokens(1) == 40
     _decode(lay, r, inps, orcs, 2, torch.bfloat16, rq, "caught-up")
+
+
+
+@pytest.mark.parametrize("retrieval_dtype", [None, "int4"])
+def test_ragged_slices_with_many_retrieval_heads_then_batch_wide(retrieval_dtype):
+    """70 ragged sequences with 8 retrieval KV heads decode in two launches
+    per step (64 + 6 sequences); then every sequence catches up to the same
+    count and the batch-wide launch runs. All three launch shapes must find
+    the split-K arrival counters and partials at the same workspace offsets
+    (laid out for the whole batch): a counter overwritten by another launch's
+    partials would leave some head's output unwritten."""
+    int4 = retrieval_dtype == "int4"
+    base = WORKLOADS["llama3_8b_int4_decode_1m" if int4 else "llama2_7b_decode_32k"]
+    # 12 KV heads of which 8 are retrieval heads; the 4-bit decode maps
+    # G * D / 32 <= 16 columns, G = 2 here
+    w = dataclasses.replace(base, n_q_heads=24 if int4 else 12, n_kv_heads=12, head_dim=128,
+                            fixed_retrieval=(0, 1, 2, 4, 5, 7, 9, 11))
+    B, steps = 70, 2
+    g = np.random.default_rng(27000)
+    contexts = [int(x) for x in g.integers(1, 160, size=B)]
+    common = max(contexts) + steps + 1  # count every sequence reaches before phase 2
+    kv = "fp16" if int4 else "bf16"
+    dtype = torch.float16 if int4 else torch.bfloat16
+    say(f"case: 70 ragged sequences, 8 retrieval heads, sliced then batch-wide "
+        f"({retrieval_dtype or kv} retrieval cache)")
+    inps, lay, orcs, r, rq = _setup(w, B, [common - steps] * B, 2 * steps, 27000, kv_dtype=kv,
+                                    retrieval_dtype=retrieval_dtype, int4=int4)
+    assert r.nr == 8
+    for b, (x, o) in enumerate(zip(inps, orcs)):
+        c = contexts[b]
+        lay.append_kv_seq(b, r.kv(to_dev(x.k[:c], dtype))[None], r.kv(to_dev(x.v[:c], dtype))[None])
+        o.append(x.k[:c], x.v[:c])
+    _decode(lay, r, inps, orcs, steps, dtype, rq, "ragged70x8 sliced")
+    for b, (x, o) in enumerate(zip(inps, orcs)):
+        c = contexts[b]
+        lay.append_kv_seq(b, r.kv(to_dev(x.k[c:common - steps], dtype))[None],
+                          r.kv(to_dev(x.v[c:common - steps], dtype))[None])
+        o.append(x.k[c:common - steps], x.v[c:common - steps])
+    assert [lay.sequence_tokens(b) for b in range(B)] == [common] * B
+    _decode(lay, r, inps, orcs, steps, dtype, rq, "ragged70x8 batch-wide", first=steps)
+    assert [lay.sequence_tokens(b) for b in range(B)] == [common + steps] * B
