@@ -32,11 +32,20 @@
  *     No call synchronises the device. The token count is tracked on the
  *     host. A duo_layer must not be used from two threads at once, and calls
  *     on one layer must be ordered (same stream, or caller-side events).
- *   - Every call validates its arguments on the host first. On any error it
- *     returns a status other than DUO_OK, enqueues nothing and leaves the
- *     layer state (token count, caches) unchanged. No C++ exception crosses
- *     this interface. DUO_ERR_HIP reports a failed launch; an earlier
- *     asynchronous device fault may surface there.
+ *   - Every call validates its arguments on the host first, including every
+ *     condition a launch of the call depends on. On any status other than
+ *     DUO_OK and DUO_ERR_HIP it enqueues nothing and leaves the layer state
+ *     (token count, caches) unchanged. No C++ exception crosses this
+ *     interface.
+ *   - DUO_ERR_HIP reports a failed launch (an earlier asynchronous device
+ *     fault may surface there). Calls made of several launches (prefill:
+ *     cache append, then attention, then ring update; append: cache, then
+ *     ring; decode of a ragged batch of more than 64 sequences: one launch
+ *     per 64) may have enqueued the launches before the one that failed.
+ *     The token count is then not advanced, but cache rows and ring slots of
+ *     the new positions may already be written, overwriting ring slots that
+ *     held older positions: the layer's caches are undefined and it must be
+ *     refilled (or destroyed) before further use.
  *   - Pointers must be 16-byte aligned (DUO_ERR_LAYOUT otherwise).
  */
 #ifndef DUO_H_
@@ -114,7 +123,7 @@ typedef struct duo_layer duo_layer; /* opaque host object */
 /* Sizes and offsets of the buffers a layer needs. Host-only; no HIP call.
  * Errors: DUO_ERR_INVALID_ARG for a null pointer or a bad descriptor,
  * DUO_ERR_UNSUPPORTED for an unsupported head_dim, group size or dtype or a
- * batch above 65535, DUO_ERR_CAPACITY when a buffer of the layout would
+ * batch or KV-head count above 65535, DUO_ERR_CAPACITY when a buffer of the layout would
  * exceed 2^62 bytes. */
 duo_status duo_layer_layout(const duo_layer_desc* desc, duo_layout* layout);
 
@@ -152,13 +161,22 @@ int64_t duo_layer_sequence_tokens(const duo_layer* layer, int32_t b);
  * at positions [n, n + n_tokens) without attending: retrieval heads write
  * their cache rows (quantising them for INT4_G32), streaming heads write the
  * ring slots of the positions that survive (the sinks and the last `recent`).
+ * Defined by: xllm-io review "DuoAttention: Efficient Long-Context LLM
+ * Inference with Retrieval and Streaming Heads", section 三 推理流程, 解码阶段
+ * (each layer keeps a full cache for retrieval heads and a sink + recent cache
+ * for streaming heads) and section 五 量化组合 (4-bit KV cache); the 4-bit
+ * group encoding itself is this library's (the pages give none).
  * Used to fill a context. DUO_ERR_CAPACITY if n + n_tokens > capacity;
  * DUO_ERR_UNSUPPORTED while the sequences hold different counts (use
  * duo_append_kv_seq). */
 duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t n_tokens,
                          hipStream_t stream);
 
-/* Chunked prefill of `chunk_len` >= 1 tokens at positions [n, n+chunk_len):
+/* Chunked prefill (xllm-io review, section 三 推理流程, 预填充阶段: chunked
+ * pre-filling, streaming heads in linear time and constant memory, retrieval
+ * heads with full attention; paperlayer summary of arXiv 2410.10819v1,
+ * section 2 Chunked Pre-filling; the masks of section 三 核心公式)
+ * of `chunk_len` >= 1 tokens at positions [n, n+chunk_len):
  * q [B, chunk_len, Hq, D] bf16, k/v [B, chunk_len, Hkv, D]. Retrieval heads
  * append the chunk to their cache and attend causally over positions
  * [0, n+chunk_len); streaming heads attend under the Lambda mask over the ring
@@ -170,7 +188,10 @@ duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t
 duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,
                              int32_t chunk_len, void* out, hipStream_t stream);
 
-/* One decode step at position n: q [B, 1, Hq, D] bf16, k_new/v_new
+/* One decode step (xllm-io review, section 三 推理流程, 解码阶段: the new
+ * token's Q/K/V split along heads, each head class attending over its own
+ * cache, outputs concatenated along heads; masks of section 三 核心公式)
+ * at position n: q [B, 1, Hq, D] bf16, k_new/v_new
  * [B, 1, Hkv, D]. The new token is appended to both caches, then every head
  * attends (retrieval: positions [0, n]; streaming: the sinks and the last
  * `recent` positions, the new one included). Writes out [B, 1, Hq, D] bf16.
@@ -193,7 +214,10 @@ duo_status duo_append_kv_seq(duo_layer* layer, int32_t b, const void* k, const v
 duo_status duo_prefill_chunk_seq(duo_layer* layer, int32_t b, const void* q, const void* k,
                                  const void* v, int32_t chunk_len, void* out, hipStream_t stream);
 
-/* Stateless gate-blended forward used for head identification:
+/* Stateless gate-blended forward used for head identification (xllm-io
+ * review, section 三 核心公式, 混合注意力, and 检索头识别: one gate per KV
+ * head blends full and Lambda-masked attention; paperlayer summary of arXiv
+ * 2410.10819v1, section 2 Optimization-based Identification):
  * out_h = alpha[h/G] * full_h + (1 - alpha[h/G]) * streaming_h over one
  * sequence of `seq_len` tokens. q [B, T, Hq, D] bf16, k/v [B, T, Hkv, D]
  * (kv_dtype must be BF16), alpha [Hkv] fp32 on the device; the descriptor's
@@ -241,7 +265,10 @@ duo_status duo_mixed_alpha_grad(const duo_layer_desc* desc, const void* q, const
                                 float l1_weight, int32_t seq_len, float* grad_alpha,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Host-only: stable permutation that makes retrieval heads contiguous.
+/* Host-only: stable permutation that makes retrieval heads contiguous
+ * (xllm-io review, section 三 模型部署优化: projection weights reordered so
+ * that retrieval and streaming heads form contiguous blocks; section 三 推理流程:
+ * the heads are split and concatenated along the head axis).
  * mask[h] != 0 marks KV head h as a retrieval head. perm_out[i] receives the
  * original KV head placed at position i (retrieval heads ascending, then
  * streaming heads ascending); *n_retrieval_out the number of retrieval
@@ -280,7 +307,10 @@ duo_status duo_reorder_head_rows(const void* in, void* out, const int32_t* perm,
                                  int64_t rows_per_head, int64_t row_bytes);
 
 /* Host-only: ring slot of token position p (the rule stated above), or -1
- * for invalid arguments. */
+ * for invalid arguments. The streaming cache holds the sinks and the most
+ * recent tokens (xllm-io review, section 三 推理流程, 解码阶段; paperlayer
+ * summary of arXiv 2410.10819v1, section 2); the ring that holds them is
+ * this library's layout. */
 int32_t duo_ring_slot(int64_t position, int32_t sink, int32_t recent);
 
 /* Static text for a status code. */

@@ -63,8 +63,9 @@ size_t ws_bytes(const duo_layer_desc& d, int max_split) {
 }
 
 WsView ws_view(const duo_layer* L) {
-  const duo_layer_desc& d = L->d;
-  size_t Hr = (size_t)L->Hr, B = (size_t)d.batch, G = (size_t)L->G;
+  // the attached layer's batch, not a view's: every view of a layer must
+  // find the counters and partials at the same offsets
+  size_t Hr = (size_t)L->Hr, B = (size_t)L->ws_batch, G = (size_t)L->G;
   size_t cnt = align_up(B * Hr * sizeof(uint32_t) + 4, 256);
   size_t ml = align_up(B * Hr * G * (size_t)L->max_split * 2 * sizeof(float), 256);
   WsView v;
@@ -87,8 +88,10 @@ static bool size_ok(std::initializer_list<size_t> factors) {
 static duo_status check_desc(const duo_layer_desc* d) {
   if (!d) return DUO_ERR_INVALID_ARG;
   if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return DUO_ERR_INVALID_ARG;
-  // the batch index is a grid dimension of at most 65535 blocks
-  if (d->batch > 65535) return DUO_ERR_UNSUPPORTED;
+  // the batch index and a cache's head index are grid dimensions of at most
+  // 65535 blocks (checked here so that no launch of a call can fail on them
+  // after an earlier launch of the same call was enqueued)
+  if (d->batch > 65535 || d->n_kv_heads > 65535) return DUO_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads) return DUO_ERR_INVALID_ARG;
   int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return DUO_ERR_UNSUPPORTED;
@@ -211,6 +214,7 @@ static duo_status layer_init(duo_layer** out, const duo_layer_desc* d, void* ret
   L->Hr = d->n_retrieval_kv_heads;
   L->Hs = d->n_kv_heads - d->n_retrieval_kv_heads;
   L->max_split = max_split_for(*d);
+  L->ws_batch = d->batch;
   int dev = 0;
   L->cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -473,11 +477,11 @@ size_t duo_mixed_alpha_grad_workspace(const duo_layer_desc* d, int32_t T) {
   return align_up(mixed_grad_partials(*d, T) * sizeof(float), 256);
 }
 
-duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* d, const void* q, const void* k,
-                                      const void* v, const void* dout, const float* alpha,
-                                      float l1_weight, int32_t T, int32_t lambda_block,
-                                      float* grad, void* ws, size_t ws_bytes,
-                                      hipStream_t stream) {
+// Checks shared by the gate-gradient calls (everything but the workspace).
+static duo_status check_alpha_grad(const duo_layer_desc* d, const void* q, const void* k,
+                                   const void* v, const void* dout, const float* alpha,
+                                   float l1_weight, int32_t T, int32_t lambda_block,
+                                   const float* grad) {
   duo_status st = check_desc(d);
   if (st != DUO_OK) return st;
   if (d->kv_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
@@ -486,11 +490,23 @@ duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* d, const void* q, co
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(dout)) != DUO_OK)
     return st;
-  if (!alpha || !grad || !ws) return DUO_ERR_INVALID_ARG;
-  if (!aligned(alpha, 4) || !aligned(grad, 4) || !aligned(ws, 16)) return DUO_ERR_LAYOUT;
-  if (ws_bytes < mixed_grad_partials(*d, T) * sizeof(float)) return DUO_ERR_INVALID_ARG;
+  if (!alpha || !grad) return DUO_ERR_INVALID_ARG;
+  if (!aligned(alpha, 4) || !aligned(grad, 4)) return DUO_ERR_LAYOUT;
   if ((int64_t)T * d->n_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
     return DUO_ERR_UNSUPPORTED;
+  return DUO_OK;
+}
+
+duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* d, const void* q, const void* k,
+                                      const void* v, const void* dout, const float* alpha,
+                                      float l1_weight, int32_t T, int32_t lambda_block,
+                                      float* grad, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  duo_status st = check_alpha_grad(d, q, k, v, dout, alpha, l1_weight, T, lambda_block, grad);
+  if (st != DUO_OK) return st;
+  if (!ws) return DUO_ERR_INVALID_ARG;
+  if (!aligned(ws, 16)) return DUO_ERR_LAYOUT;
+  if (ws_bytes < mixed_grad_partials(*d, T) * sizeof(float)) return DUO_ERR_INVALID_ARG;
   if (launch_mixed_alpha_grad(*d, q, k, v, dout, alpha, l1_weight, T, lambda_block, grad,
                               static_cast<float*>(ws), stream) != hipSuccess)
     return DUO_ERR_HIP;

@@ -73,10 +73,11 @@ def test_layout_sizes():
     (dict(kv_dtype="fp16", retrieval_dtype="int4", capacity=(1 << 25)), 2),
     # 16-bit cache: one head's rows plus 32 padding rows must stay below 2^31 bytes
     (dict(capacity=(1 << 23)), 2),
-    # the batch is a grid dimension
+    # the batch and the KV heads are grid dimensions
     (dict(batch=65536), 2),
-    # sizes whose byte counts would not fit: 65535 x (2^31 - 1) heads x 2^22 rows
-    (dict(batch=65535, n_q_heads=(1 << 31) - 1, n_kv_heads=(1 << 31) - 1,
+    (dict(n_q_heads=65536, n_kv_heads=65536, n_retrieval_kv_heads=4), 2),
+    # sizes whose byte counts would not fit: 65535 x 65535 heads x 2^22 rows
+    (dict(batch=65535, n_q_heads=65535, n_kv_heads=65535,
           n_retrieval_kv_heads=1, capacity=(1 << 22)), 4),
 ])
 def test_bad_descriptor_rejected(kw, status):
