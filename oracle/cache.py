@@ -25,6 +25,31 @@ from .attention import masked_attention
 from .int4 import quantize_int4_g32, dequantize_int4_g32
 
 
+class _Rows:
+    """Rows of one head's retrieval cache in a float64 array that grows by
+    doubling (storage only: the rows are kept exactly as appended)."""
+
+    def __init__(self, width):
+        self.buf = np.empty((16, width), np.float64)
+        self.n = 0
+
+    def extend(self, rows):
+        rows = np.asarray(rows, np.float64).reshape(-1, self.buf.shape[1])
+        need = self.n + rows.shape[0]
+        if need > self.buf.shape[0]:
+            grown = np.empty((max(need, 2 * self.buf.shape[0]), self.buf.shape[1]), np.float64)
+            grown[:self.n] = self.buf[:self.n]
+            self.buf = grown
+        self.buf[self.n:need] = rows
+        self.n = need
+
+    def rows(self):
+        return self.buf[:self.n]
+
+    def __len__(self):
+        return self.n
+
+
 def ring_slot(p: int, sink: int, recent: int) -> int:
     return p if p < sink else sink + (p - sink) % recent
 
@@ -54,9 +79,9 @@ class OracleLayer:
         self.scale, self.S, self.R = scale, sink, recent
         self.int4 = int4
         self.n = 0
-        # retrieval heads: list of per-token rows (values the attention reads)
-        self.full_k = {h: [] for h in range(n_kv_heads) if self.mask[h]}
-        self.full_v = {h: [] for h in range(n_kv_heads) if self.mask[h]}
+        # retrieval heads: the rows the attention reads, in position order
+        self.full_k = {h: _Rows(head_dim) for h in range(n_kv_heads) if self.mask[h]}
+        self.full_v = {h: _Rows(head_dim) for h in range(n_kv_heads) if self.mask[h]}
         # int4 encodings kept for byte-level comparison: per head lists of (codes, s, z)
         self.enc_k = {h: [] for h in self.full_k}
         self.enc_v = {h: [] for h in self.full_k}
@@ -72,23 +97,25 @@ class OracleLayer:
             self.enc_v[h].append((cv, sv, zv))
             k_rows = dequantize_int4_g32(ck, sk, zk)
             v_rows = dequantize_int4_g32(cv, sv, zv)
-        self.full_k[h].extend(np.asarray(k_rows, np.float64))
-        self.full_v[h].extend(np.asarray(v_rows, np.float64))
+        self.full_k[h].extend(k_rows)
+        self.full_v[h].extend(v_rows)
+
+    def _store_ring(self, k, v):
+        """Position-ordered writes of tokens n..n+T-1 into the streaming rings."""
+        for h in self.ring:
+            for t in range(k.shape[0]):
+                p = self.n + t
+                self.ring[h][ring_slot(p, self.S, self.R)] = (
+                    p, np.asarray(k[t, h], np.float64), np.asarray(v[t, h], np.float64))
 
     def append(self, k, v):
         """Append tokens n..n+T-1 to both caches (no attention). k/v [T,Hkv,D]."""
         k = np.asarray(k)
         v = np.asarray(v)
-        T = k.shape[0]
-        for h in range(self.Hkv):
-            if self.mask[h]:
-                self._store_retrieval(h, k[:, h], v[:, h])
-            else:
-                for t in range(T):
-                    p = self.n + t
-                    self.ring[h][ring_slot(p, self.S, self.R)] = (
-                        p, np.asarray(k[t, h], np.float64), np.asarray(v[t, h], np.float64))
-        self.n += T
+        for h in self.full_k:
+            self._store_retrieval(h, k[:, h], v[:, h])
+        self._store_ring(k, v)
+        self.n += k.shape[0]
 
     def ring_contents(self, h):
         """slot -> position for streaming head h (-1 = empty)."""
@@ -111,17 +138,12 @@ class OracleLayer:
         out = np.full((T, self.Hq, self.D), np.nan)
         for kvh in range(self.Hkv):
             if self.mask[kvh]:
-                if self.int4:
-                    ck, sk, zk = quantize_int4_g32(k[:, kvh])
-                    cv, sv, zv = quantize_int4_g32(v[:, kvh])
-                    kc = dequantize_int4_g32(ck, sk, zk).astype(np.float64)
-                    vc = dequantize_int4_g32(cv, sv, zv).astype(np.float64)
-                else:
-                    kc, vc = k[:, kvh], v[:, kvh]
-                old_k = np.array(self.full_k[kvh]).reshape(-1, self.D)
-                old_v = np.array(self.full_v[kvh]).reshape(-1, self.D)
-                keys = np.concatenate([old_k, kc])
-                vals = np.concatenate([old_v, vc])
+                # the chunk joins the full cache first (4-bit caches hold its
+                # decoded values), then its queries attend over positions
+                # 0..n+T-1
+                self._store_retrieval(kvh, k[:, kvh], v[:, kvh])
+                keys = self.full_k[kvh].rows()
+                vals = self.full_v[kvh].rows()
                 k_pos = np.arange(self.n + T)
                 kind = "full"
             else:
@@ -134,7 +156,9 @@ class OracleLayer:
                 h = kvh * self.G + g
                 out[rows, h] = masked_attention(q[rows, h], keys, vals, chunk_pos[rows], k_pos,
                                                 self.scale, kind, self.S, self.R)
-        self.append(k, v)
+        # the rings are updated after every streaming head has read them
+        self._store_ring(k, v)
+        self.n += T
         return out
 
     def decode(self, q, k, v):
