@@ -120,3 +120,36 @@ def grad_tolerance(q, k, v, dout, scale, S, R, block=0):
             var[kv] += np.sum((w * dv) ** 2)
             mass[kv] += np.sum(np.abs(dout[:, h] * o))
     return 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass
+
+
+def grad_tolerance_rows(q, k, v, dout, scale, S, R, kv_heads, rows_per_block=1024):
+    """grad_tolerance for the KV heads ``kv_heads`` only, over query rows in
+    blocks (each block sees keys up to its last row), for sequences too long
+    for one T x T matrix. Returns {kv head: bound}."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = {}
+    for kv in kv_heads:
+        var = mass = 0.0
+        for h in range(kv * G, kv * G + G):
+            for r0 in range(0, T, rows_per_block):
+                r1 = min(T, r0 + rows_per_block)
+                i = np.arange(r0, r1)[:, None]
+                j = np.arange(r1)[None, :]
+                kk = np.asarray(k[:r1, kv], np.float64)
+                vv = np.asarray(v[:r1, kv], np.float64)
+                dd = np.asarray(dout[r0:r1, h], np.float64)
+                s = scale * np.asarray(q[r0:r1, h], np.float64) @ kk.T
+                causal = j <= i
+                for allowed in (causal, causal & ((j < S) | (i - j < R))):
+                    z = np.where(allowed, s, -np.inf)
+                    z -= z.max(axis=1, keepdims=True)
+                    w = np.exp(z)
+                    w /= w.sum(axis=1, keepdims=True)
+                    o = w @ vv
+                    dv = dd @ vv.T - np.sum(dd * o, axis=1, keepdims=True)
+                    var += float(np.sum((w * dv) ** 2))
+                    mass += float(np.sum(np.abs(dd * o)))
+        out[kv] = 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass
+    return out

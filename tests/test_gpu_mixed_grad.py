@@ -13,7 +13,9 @@ accumulation, and compare with the oracle: several group sizes and head
 dims, ragged lengths, no sinks, a window covering the sequence, a batch of
 two distinct sequences, and the gates' L1 term (positive, zero and negative
 gates). At the Llama-2-7B identification size (16384 tokens, 32 heads) the
-oracle is too slow; there the gradient must equal the forward difference
+oracle gives the gradient of two KV heads, composed from its full and
+streaming attention over blocks of query rows, within the same bound; and
+every head's gradient must equal the forward difference
 sum(dout * (mixed(alpha=1) - mixed(alpha=0))) taken from the forward kernel,
 which rounds P identically, so only the forward's bf16 output rounding (at
 most 2^-9 relative, independent) separates the two.
@@ -26,7 +28,7 @@ import torch
 
 import oracle
 from duo_synth import WORKLOADS, device_normal, normal, random_case, rng, round_bf16
-from gpu_util import device, grad_tolerance, say, to_dev
+from gpu_util import device, grad_tolerance, grad_tolerance_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +121,43 @@ def test_alpha_grad_full_size_forward_difference():
     say(f"  max |grad - fd| = {err.max().item():.3e}, min bound {bound.min().item():.3e}, "
         f"max |fd| = {fd.abs().max().item():.3e}")
     assert torch.all(err <= bound), (g, fd, bound)
+
+
+def test_alpha_grad_full_size_against_oracle():
+    """The 16384-token MHA 32x128 identification layer, inputs drawn on the
+    host: the gradient of KV heads 3 and 26 from the oracle, as the sum over
+    the tokens and channels of dout * (full - streaming), each attention taken
+    from oracle.masked_attention over blocks of 1024 query rows (a block's
+    keys are the positions up to its last row; the masks remove the rest)."""
+    import kv_cache_compression_duo_amd as duo
+    dev = device()
+    w = WORKLOADS["llama2_7b_mixed_16k"]
+    T, H, D = w.mixed_tokens, w.n_q_heads, w.head_dim
+    S, R, scale, l1 = w.sink, w.recent, w.softmax_scale, 0.05
+    heads = (3, 26)
+    say(f"case: alpha grad full size T={T} H={H} D={D}, heads {heads} against the oracle")
+    g = rng(19100)
+    q = round_bf16(normal(g, (T, H, D)))
+    k = round_bf16(normal(g, (T, H, D)))
+    v = round_bf16(normal(g, (T, H, D)))
+    dout = round_bf16(normal(g, (T, H, D)))
+    alpha = g.uniform(0.0, 1.0, size=H).astype(np.float32)
+    got = _gpu_grad([q], [k], [v], [dout], alpha, scale, S, R, l1)
+    pos = np.arange(T)
+    ref = {}
+    for h in heads:
+        acc = 0.0
+        for r0 in range(0, T, 1024):
+            rows = pos[r0:r0 + 1024]
+            hi = rows[-1] + 1
+            full = oracle.masked_attention(q[rows, h], k[:hi, h], v[:hi, h], rows, pos[:hi],
+                                           scale, "full")
+            stream = oracle.masked_attention(q[rows, h], k[:hi, h], v[:hi, h], rows, pos[:hi],
+                                             scale, "streaming", S, R)
+            acc += float(np.sum(dout[rows, h].astype(np.float64) * (full - stream)))
+        ref[h] = acc + l1 * float(np.sign(alpha[h]))
+    tol = grad_tolerance_rows(q, k, v, dout, scale, S, R, heads)
+    for h in heads:
+        say(f"  head {h}: gpu {got[h]:.6f} oracle {ref[h]:.6f} |diff| "
+            f"{abs(got[h] - ref[h]):.3e} bound {tol[h]:.3e}")
+        assert abs(got[h] - ref[h]) <= tol[h], (h, got[h], ref[h], tol[h])
