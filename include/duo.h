@@ -284,6 +284,28 @@ duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* desc, const void* q,
                                       float* grad_alpha, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* Partial-sum slots of duo_mixed_alpha_grad_noalloc: one per attention block
+ * of the flash kernel, B * Hkv * ceil(seq_len / 256) for G = 1,
+ * B * Hkv * (G / 2) * ceil(seq_len / 128) for G = 2, and
+ * B * Hkv * (G / 4) * ceil(seq_len / 64) for G = 4 or 8 (what
+ * duo_mixed_alpha_grad_workspace reports, in floats). */
+#define DUO_GRAD_SCRATCH_PARTIALS 65536
+
+/* duo_mixed_alpha_grad_block without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid hipMalloc). The per-block partial sums go to a file-scope
+ * device array of DUO_GRAD_SCRATCH_PARTIALS floats (256 KiB) that each device
+ * the library runs on holds until the process ends; its address is looked up
+ * on the first call on a device. A launch needing more partial slots returns
+ * DUO_ERR_CAPACITY (use duo_mixed_alpha_grad_block with a workspace). Calls
+ * on one device share that array: calls that overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller. Nothing
+ * is allocated; other arguments and errors as for duo_mixed_alpha_grad_block. */
+duo_status duo_mixed_alpha_grad_noalloc(const duo_layer_desc* desc, const void* q, const void* k,
+                                        const void* v, const void* dout, const float* alpha,
+                                        float l1_weight, int32_t seq_len, int32_t lambda_block,
+                                        float* grad_alpha, hipStream_t stream);
+
 /* Host-only: retrieval mask from trained gates (xllm-io review, section 三
  * 检索头识别, step 3: alpha is binarized as 1[alpha >= tau]; paperlayer
  * summary, section 2, Binarizing Attention Implementations: tau is the

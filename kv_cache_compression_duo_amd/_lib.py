@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libduo.so")
 
 DUO_OK, DUO_ERR_INVALID_ARG, DUO_ERR_UNSUPPORTED, DUO_ERR_LAYOUT, DUO_ERR_CAPACITY, DUO_ERR_HIP = range(6)
 DUO_BF16, DUO_FP16, DUO_INT4_G32 = 0, 1, 2
+DUO_GRAD_SCRATCH_PARTIALS = 65536  # slots of duo_mixed_alpha_grad_noalloc's device array
 DTYPES = {"bf16": DUO_BF16, "fp16": DUO_FP16, "int4": DUO_INT4_G32}
 
 
@@ -74,6 +75,9 @@ def _load():
         "duo_mixed_alpha_grad_block": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
                                                c_void_p, c_void_p, c_float, c_int32, c_int32,
                                                c_void_p, c_void_p, c_size_t, c_void_p]),
+        "duo_mixed_alpha_grad_noalloc": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_float, c_int32, c_int32,
+                                                 c_void_p, c_void_p]),
         "duo_mixed_alpha_grad_workspace": (c_size_t, [POINTER(LayerDesc), c_int32]),
         "duo_mixed_alpha_grad": (c_int, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_float, c_int32, c_void_p,

@@ -276,6 +276,34 @@ def mixed_alpha_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: to
     return grad
 
 
+def mixed_alpha_grad_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             dout: torch.Tensor, alpha: torch.Tensor, grad: torch.Tensor, *,
+                             softmax_scale: float, sink: int = 16, recent: int = 64,
+                             l1_weight: float = 0.0, lambda_block: int = 0):
+    """mixed_alpha_grad through the entry point that allocates nothing: the
+    per-block partial sums live in the library's device array (calls that
+    overlap on one device race). The caller passes the output ``grad``
+    [Hkv] fp32; a launch needing more than DUO_GRAD_SCRATCH_PARTIALS partial
+    slots raises DuoError (status DUO_ERR_CAPACITY)."""
+    dev = _gpu(q.device)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _check_act(q, "q", (B, T, Hq, D), torch.bfloat16, dev)
+    _check_act(k, "k", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(v, "v", (B, T, Hkv, D), torch.bfloat16, dev)
+    _check_act(dout, "dout", (B, T, Hq, D), torch.bfloat16, dev)
+    _check_act(alpha, "alpha", (Hkv,), torch.float32, dev)
+    _check_act(grad, "grad", (Hkv,), torch.float32, dev)
+    desc = make_desc(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=0,
+                     sink=sink, recent=recent, capacity=0, softmax_scale=softmax_scale)
+    with torch.cuda.device(dev):
+        check(lib.duo_mixed_alpha_grad_noalloc(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                               _ptr(alpha), float(l1_weight), T,
+                                               int(lambda_block), _ptr(grad), _stream_ptr(dev)),
+              "duo_mixed_alpha_grad_noalloc")
+    return grad
+
+
 def binarize_gates(alpha, sparsity: float):
     """Retrieval mask (list of 0/1, 1 = retrieval) from trained gates (host
     call): the floor(sparsity * n) smallest gates become streaming heads,

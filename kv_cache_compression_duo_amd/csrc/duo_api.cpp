@@ -513,6 +513,21 @@ duo_status duo_mixed_alpha_grad_block(const duo_layer_desc* d, const void* q, co
   return DUO_OK;
 }
 
+duo_status duo_mixed_alpha_grad_noalloc(const duo_layer_desc* d, const void* q, const void* k,
+                                        const void* v, const void* dout, const float* alpha,
+                                        float l1_weight, int32_t T, int32_t lambda_block,
+                                        float* grad, hipStream_t stream) {
+  duo_status st = check_alpha_grad(d, q, k, v, dout, alpha, l1_weight, T, lambda_block, grad);
+  if (st != DUO_OK) return st;
+  if (mixed_grad_partials(*d, T) > kGradScratchPartials) return DUO_ERR_CAPACITY;
+  float* partial = nullptr;
+  if (grad_scratch(&partial) != hipSuccess) return DUO_ERR_HIP;
+  if (launch_mixed_alpha_grad(*d, q, k, v, dout, alpha, l1_weight, T, lambda_block, grad,
+                              partial, stream) != hipSuccess)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
 duo_status duo_mixed_alpha_grad(const duo_layer_desc* d, const void* q, const void* k,
                                 const void* v, const void* dout, const float* alpha,
                                 float l1_weight, int32_t T, float* grad, void* ws,

@@ -73,6 +73,11 @@ hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const
                                    const void* v, const void* dout, const float* alpha,
                                    float l1_weight, int T, int lam_block, float* grad,
                                    float* partial, hipStream_t s);
+// Partial slots of the allocation-free gate gradient (a file-scope device
+// array; duo_mixed_alpha_grad_noalloc refuses larger launches).
+constexpr size_t kGradScratchPartials = DUO_GRAD_SCRATCH_PARTIALS;
+// Address of the current device's copy of that array (looked up on first use).
+hipError_t grad_scratch(float** out);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace duo

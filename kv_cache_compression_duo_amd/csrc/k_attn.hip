@@ -36,6 +36,8 @@
 //     that both MFMA operands are read with one ds_read_b128 each;
 //   * the next tile's global loads are in flight while the current tile is
 //     computed; query tiles are launched longest-first (causal imbalance).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "duo_internal.hpp"
 
@@ -704,6 +706,38 @@ size_t mixed_grad_partials(const duo_layer_desc& d, int T) {
   const int G = d.n_q_heads / d.n_kv_heads, HB = heads_per_block(G);
   const int BMT = 32 * 8 / HB;
   return (size_t)d.batch * d.n_kv_heads * (G / HB) * (size_t)((T + BMT - 1) / BMT);
+}
+
+// Partials of the allocation-free gate gradient: one fp32 sum per flash block,
+// in a file-scope device array instead of a caller workspace. Every device the
+// library runs on holds its own copy until the process ends; every call on a
+// device shares it, so calls that overlap on one device race.
+static __device__ __align__(256) float scratch[kGradScratchPartials];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current). In host code the array's name is only a
+// stand-in: kernels must be given this address.
+hipError_t grad_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const void* k,
