@@ -7,7 +7,7 @@
 
 namespace duo {
 
-constexpr int kTile = 32;  // rows per wave-tile
+constexpr int kTile = 16;  // rows per wave-tile
 
 // Per-wave online-softmax state for G query heads over 8 channels per lane.
 template <int G>
@@ -168,7 +168,7 @@ __device__ __forceinline__ float dot8(const QFrag<G>& q, int g, const u32x4& k) 
 // [16 l, 16 l + 16) of it from a wave-uniform base and the loads need no
 // per-lane arithmetic and no branch (a branch around loads would make the
 // compiler drain the prefetch at the join). A tile starts at min(t, r1 - 1)
-// and reads 32 rows from there: the cache buffer extends kDecodePadRows rows
+// and reads kTile rows from there: the cache buffer extends kDecodePadRows rows
 // past its last row, so this stays in bounds; rows at or past r1 (any bytes)
 // are masked and their values zeroed in the one partial tile of the range.
 // Tiles are interleaved across the block's waves with the next tile's loads
@@ -177,7 +177,7 @@ __device__ __forceinline__ float dot8(const QFrag<G>& q, int g, const u32x4& k) 
 // slab_bytes is the byte range readable from kc (and from vc): the head's
 // rows plus the padding, below 2^31. On return l and acc are summed over the
 // wave's rows; m is the wave maximum.
-template <int D, int G, typename Tag, int NW>
+template <int D, int G, typename Tag, int NW, int PF = 2>
 __device__ __forceinline__ void attend_cache(WaveState<G>& st, const QFrag<G>& q, float sscale,
                                              const uint16_t* __restrict__ kc,
                                              const uint16_t* __restrict__ vc,
@@ -273,19 +273,23 @@ __device__ __forceinline__ void attend_cache(WaveState<G>& st, const QFrag<G>& q
       }
       update(s, vb, U);
     };
+    // PF register buffers in a ring: while tile j is computed the loads of
+    // tiles j + 1 .. j + PF - 1 are in flight (prefetches past the range
+    // clamp to its last row: a cached re-read, never computed)
     constexpr int stride = NW * kTile;
-    u32x4 ka[U], va[U], kb[U], vb[U];
-    load(ka, va, t0);
+    u32x4 kq[PF][U], vq[PF][U];
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p) load(kq[p], vq[p], t0 + p * stride);
     for (;;) {
-      const int t1 = t0 + stride;
-      load(kb, vb, t1);
-      compute(ka, va, t0);
-      if (t1 >= r1) break;
-      t0 = t1 + stride;
-      load(ka, va, t0);
-      compute(kb, vb, t1);
-      if (t0 >= r1) break;
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        load(kq[(p + PF - 1) % PF], vq[(p + PF - 1) % PF], t0 + (p + PF - 1) * stride);
+        compute(kq[p], vq[p], t0 + p * stride);
+        if (t0 + (p + 1) * stride >= r1) goto tiles_done;  // wave-uniform
+      }
+      t0 += PF * stride;
     }
+  tiles_done:;
   }
   if (with_new && wave == 0) {
     // one more row: lanes of row slot 0 carry it, the others are masked
@@ -321,8 +325,9 @@ __device__ __forceinline__ void attend_cache(WaveState<G>& st, const QFrag<G>& q
 // Merge the waves' states through LDS. On return, thread t < G*D/8... holds
 // nothing; the merged (m, l, acc[D]) per head is left in LDS `red`.
 template <int D, int G, int NW>
-struct BlockRed {
-  float m[NW][G], l[NW][G], acc[NW][G][D];
+struct alignas(16) BlockRed {
+  float acc[NW][G][D];  // first: rows of acc[0] are read as 16-byte vectors
+  float m[NW][G], l[NW][G];
   float M[G], L[G];
 };
 

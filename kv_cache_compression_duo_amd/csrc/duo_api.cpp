@@ -116,6 +116,10 @@ static duo_status check_desc(const duo_layer_desc* d) {
         !size_ok({B, (size_t)d->n_kv_heads, G, (size_t)max_split_for(*d), D + 2, 4}))
       return DUO_ERR_CAPACITY;
   }
+  // the split-K partials of one (sequence, KV head) are addressed with 32-bit
+  // byte offsets (implied by the cache limits below; checked here as well)
+  if ((int64_t)G * max_split_for(*d) * (d->head_dim + 2) * 4 >= ((int64_t)1 << 31))
+    return DUO_ERR_UNSUPPORTED;
   // the 4-bit decode kernel maps (query head, channel group) pairs of a KV
   // head onto the 16 columns of one MFMA tile
   if (d->retrieval_dtype == DUO_INT4_G32 && G * (d->head_dim / 32) > 16) return DUO_ERR_UNSUPPORTED;

@@ -32,7 +32,7 @@ constexpr int kMinSplitTokens = 256;  // smallest split-K range (tokens)
 // decode kernels in their arguments: at most this many sequences.
 constexpr int kMaxRaggedBatch = 64;
 // Rows of readable (never used) memory after a bf16/fp16 retrieval buffer: a
-// decode tile of 32 rows starting at any valid row stays inside the buffer.
+// decode tile (at most 32 rows) starting at any valid row stays inside the buffer.
 constexpr int kDecodePadRows = 32;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

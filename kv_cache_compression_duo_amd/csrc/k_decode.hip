@@ -13,7 +13,7 @@
 // 4, FlashDecoding); the partials here are merged by the last block to finish.
 //
 // Design for gfx950: decode is bound by HBM reads of the retrieval cache. A
-// wave streams 32 cache rows per tile with 16-byte loads (D/8 lanes per row,
+// wave streams 16 cache rows per tile with 16-byte loads (D/8 lanes per row,
 // rows contiguous in memory), K and V loads of a tile are issued together, and
 // the G query heads of a KV head share every K/V load. Scores are reduced
 // across the lanes of a row with DPP; only the tile maximum crosses rows.
@@ -37,7 +37,7 @@ struct DecodeArgs {
   uint16_t* vc;
   uint16_t* kr;           // [B][Hs][W][D]
   uint16_t* vr;
-  uint32_t* counters;     // [B][Hr]
+  uint32_t* counters;     // arrival counts [B][Hr]
   float* ml;              // [B][Hr][G][max_split][2]
   float* acc;             // [B][Hr][G][max_split][D]
   int Hq, Hkv, Hr, Hs, S, R, max_split;
@@ -51,15 +51,18 @@ struct DecodeArgs {
   int nseq[kMaxRaggedBatch];  // position of the new token per sequence
 };
 
-constexpr int kDecodeWaves = 4;  // waves per block
+// Waves per block and tiles per wave held in registers (measured on the
+// Llama-2 layer: 8 or 16 waves per block, or 3 or 4 tiles in flight per wave,
+// were slower than 4 waves with 2 tiles of 16 rows).
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodePrefetch = 2;
 
 template <int D, int G, typename Tag>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;
   constexpr int NW = kDecodeWaves;
+  constexpr int PF = kDecodePrefetch;
   __shared__ BlockRed<D, G, NW> red;
-  __shared__ MergeLds<64 * NW> mlds;
-  __shared__ int is_last;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int lc = lane % LPR;
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       for (int c = 0; c < 8; ++c) qfrag.f[g][c] = qf[g][c];
     }
     const uint32_t slab_bytes = (uint32_t)((a.cap + kDecodePadRows) * D * 2);
-    attend_cache<D, G, Tag, NW>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, slab_bytes,
+    attend_cache<D, G, Tag, NW, PF>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, slab_bytes,
                                 r0, has_new ? n : r1, knew, vnew, has_new);
     // the new token's cache row (read by no block of this launch)
     if (split == 0 && threadIdx.x < LPR) {
@@ -117,33 +120,24 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
     block_merge<D, G, NW>(red, st);
     // Publish this split's partial state. The partials are written and read
-    // with agent-scope (cache-coherent) accesses and the writes are drained
-    // before the arrival count is bumped, so no cache-wide writeback or
-    // invalidate is needed on this path.
+    // with device-coherent accesses and the writes complete before the arrival
+    // count is bumped, so no cache-wide writeback or invalidate is needed on
+    // this path; the last block of the head to arrive merges.
     const int64_t pbase = (hb * G) * a.max_split;
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-      int g = i / D, dd = i % D;
-      __hip_atomic_store(a.acc + (pbase + (int64_t)g * a.max_split + split) * D + dd,
-                         red.acc[0][g][dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (threadIdx.x < G) {
-      int g = threadIdx.x;
-      float* mlp = a.ml + (pbase + (int64_t)g * a.max_split + split) * 2;
-      __hip_atomic_store(mlp, red.M[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(mlp + 1, red.L[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    const PartialView pv = partial_view<D, G>(a.ml + pbase * 2, a.acc + pbase * D, a.max_split);
+    publish_partial<D, G>(pv, a.max_split, split, &red.acc[0][0][0], red.M, red.L);
     __syncthreads();
+    __shared__ int is_last;
     if (threadIdx.x == 0) {
-      uint32_t prev = __hip_atomic_fetch_add(a.counters + hb, 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      is_last = (prev == (uint32_t)(a.n_split - 1));
+      const uint32_t prev = __hip_atomic_fetch_add(a.counters + hb, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      is_last = prev == (uint32_t)(a.n_split - 1);
     }
     __syncthreads();
     if (!is_last) return;
-    // last block of this head: merge all splits
-    merge_splits<D, G, 64 * NW>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
-                       a.out + ((int64_t)b * a.Hq + kvh * G) * D);
+    __shared__ MergeLds<64 * NW> mlds;
+    merge_splits<D, G, 64 * NW>(mlds, pv, a.max_split, a.n_split,
+                                a.out + ((int64_t)b * a.Hq + kvh * G) * D);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + hb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {

@@ -529,18 +529,8 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
 
   // ---- publish the split's partial, last block merges ------------------------
   const int64_t pbase = (hb * G) * a.max_split;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int g = i / D, dd = i % D;
-    __hip_atomic_store(a.acc + (pbase + (int64_t)g * a.max_split + split) * D + dd,
-                       red.acc[0][g][dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float* mlp = a.ml + (pbase + (int64_t)g * a.max_split + split) * 2;
-    __hip_atomic_store(mlp, red.M[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(mlp + 1, red.L[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  const PartialView pv = partial_view<D, G>(a.ml + pbase * 2, a.acc + pbase * D, a.max_split);
+  publish_partial<D, G>(pv, a.max_split, split, &red.acc[0][0][0], red.M, red.L);
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t prev = __hip_atomic_fetch_add(a.counters + hb, 1u, __ATOMIC_RELAXED,
@@ -549,7 +539,7 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   }
   __syncthreads();
   if (!is_last) return;
-  merge_splits<D, G, 64 * NW>(mlds, a.ml + pbase * 2, a.acc + pbase * D, a.max_split, a.n_split,
+  merge_splits<D, G, 64 * NW>(mlds, pv, a.max_split, a.n_split,
                      a.out + ((int64_t)b * a.Hq + kvh * G) * D);
   if (threadIdx.x == 0)
     __hip_atomic_store(a.counters + hb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

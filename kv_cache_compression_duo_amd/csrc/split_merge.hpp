@@ -1,97 +1,162 @@
-// Log-sum-exp merge of split-K partial softmax states, run by the last block
-// of a (batch, KV head) to finish. A split s holds (m_s, l_s, a_s[D]) with
-// scores in the log2 domain: m_s = max score, l_s = sum 2^(score - m_s),
+// Publication and log-sum-exp merge of split-K partial softmax states. Every
+// split block of a (batch, KV head) publishes its state; the last block to
+// arrive merges them. A split s holds (m_s, l_s, a_s[D]) with scores in the
+// log2 domain: m_s = max score, l_s = sum 2^(score - m_s),
 // a_s = sum 2^(score - m_s) v. The merged output is
 //   o = sum_s 2^(m_s - M) a_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s.
-// All threads of the block take part. Partials are read with agent-scope
-// loads, which see the other blocks' agent-scope stores without a cache
-// invalidate.
+// Partials are written and read with device-coherent (agent-scope) accesses,
+// so the merging block sees the other blocks' partials without a cache
+// writeback or invalidate. They move in 16-byte accesses: a merge issues a
+// few loads per thread instead of one per split and channel (its round trip
+// is on the critical path of the step).
 #pragma once
 #include "device_common.hpp"
 
 namespace duo {
 
-// Scratch of a merge by a block of NT threads.
+// Cache policy of a device-coherent access on this target (SC1: the bits the
+// compiler sets for agent-scope atomic loads and stores).
+constexpr int kCpolAgent = 16;
+
+__device__ __forceinline__ float4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kCpolAgent);
+  return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                     __uint_as_float(x.w));
+}
+__device__ __forceinline__ float2 ld_agent8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+  const v2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kCpolAgent);
+  return make_float2(__uint_as_float(x.x), __uint_as_float(x.y));
+}
+__device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t voff, float4 v) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 x = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, 0, kCpolAgent);
+}
+__device__ __forceinline__ void st_agent8(__amdgpu_buffer_rsrc_t r, uint32_t voff, float2 v) {
+  typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+  const v2 x = {__float_as_uint(v.x), __float_as_uint(v.y)};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)voff, 0, kCpolAgent);
+}
+
+// The partials of one (batch, KV head): ml [G][max_split][2] and acc
+// [G][max_split][D] floats (each below 2^31 bytes, checked on the host).
+struct PartialView {
+  __amdgpu_buffer_rsrc_t ml, acc;
+};
+template <int D, int G>
+__device__ __forceinline__ PartialView partial_view(float* ml, float* acc, int max_split) {
+  PartialView v;
+  v.ml = wave_rsrc(ml, (uint32_t)(G * max_split * 2 * 4));
+  v.acc = wave_rsrc(acc, (uint32_t)(G * max_split * D * 4));
+  return v;
+}
+
+// Publish split `split`'s state: acc0 [G][D] (block-shared), M[G], L[G].
+// Returns once the stores have completed (the caller then signals arrival).
+template <int D, int G>
+__device__ __forceinline__ void publish_partial(const PartialView& pv, int max_split, int split,
+                                                const float* acc0, const float* M,
+                                                const float* L) {
+  constexpr int Q = D / 4;
+  for (int i = threadIdx.x; i < G * Q; i += blockDim.x) {
+    const int g = i / Q, c4 = i % Q;
+    const float4 v = *reinterpret_cast<const float4*>(acc0 + g * D + 4 * c4);
+    st_agent16(pv.acc, (uint32_t)(((g * max_split + split) * D + 4 * c4) * 4), v);
+  }
+  if ((int)threadIdx.x < G) {
+    const int g = threadIdx.x;
+    st_agent8(pv.ml, (uint32_t)((g * max_split + split) * 8), make_float2(M[g], L[g]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the stores have reached the coherent level
+}
+
+// Scratch of a merge by a block of NT threads: a running state per thread.
 template <int NT>
 struct MergeLds {
-  float w[2 * NT];
-  float part[NT];
+  float m[NT], l[NT];
+  float4 o[NT];
 };
 
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 ld_agent2(const float* p) {  // 8-byte aligned
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-// ml: [G][max_split][2], acc: [G][max_split][D]; out row g at out + g*D (bf16).
-// Thread (part, d) folds the splits part, part + P, ... into a running
-// (m, l, o). D is a multiple of 64, so `part` is uniform in a wave and the
-// split indices and addresses are scalar. Loads are issued UN splits at a
-// time with clamped (always valid) indices, so a batch costs one memory round
-// trip; entries past the last split get weight 0. The P parts of each channel
-// are then folded in LDS.
+// Merge the n_split partials into out row g at out + g*D (bf16). Thread
+// (part, c4) folds the splits part, part + P, ... for channels 4*c4..4*c4+3:
+// each split costs it one 16-byte acc load and one 8-byte (m, l) load, issued
+// UN splits at a time with clamped (always valid) indices so that a batch is
+// one memory round trip; entries past the last split get weight 0. The P
+// parts of each channel quadruple are then folded through LDS.
 template <int D, int G, int NT>
-__device__ void merge_splits(MergeLds<NT>& s, const float* __restrict__ ml,
-                             const float* __restrict__ acc, int max_split, int n_split,
+__device__ void merge_splits(MergeLds<NT>& s, const PartialView& pv, int max_split, int n_split,
                              uint16_t* __restrict__ out) {
-  constexpr int P = NT / D;  // threads per output channel
-  constexpr int UN = 16;
-  static_assert(D % 64 == 0, "a wave must not straddle two parts");
+  constexpr int Q = D / 4;   // 16-byte columns of a partial row
+  constexpr int P = NT / Q;  // splits folded in parallel
+  constexpr int UN = 4;
+  static_assert(NT % Q == 0, "whole partial rows per pass");
   const int t = threadIdx.x;
-  const int d = t % D;
-  const int part = __builtin_amdgcn_readfirstlane(t / D);
+  const int c4 = t % Q, part = t / Q;
   for (int g = 0; g < G; ++g) {
-    const float* mlg = ml + (int64_t)g * max_split * 2;
-    const float* ag = acc + (int64_t)g * max_split * D + d;
-    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int sp0 = part; sp0 < n_split; sp0 += UN * P) {
       float2 mlv[UN];
-      float aa[UN];
+      float4 av[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int sp = sp0 + u * P < n_split ? sp0 + u * P : n_split - 1;
-        mlv[u] = ld_agent2(mlg + sp * 2);
-        aa[u] = ld_agent(ag + (int64_t)sp * D);
+        const int row = g * max_split + sp;
+        mlv[u] = ld_agent8(pv.ml, (uint32_t)(row * 8));
+        av[u] = ld_agent16(pv.acc, (uint32_t)((row * D + 4 * c4) * 4));
       }
       float mx = m;
 #pragma unroll
-      for (int u = 0; u < UN; ++u) mx = fmaxf(mx, mlv[u].x);
+      for (int u = 0; u < UN; ++u)
+        if (sp0 + u * P < n_split) mx = fmaxf(mx, mlv[u].x);
       // a split with no row (m = -inf: past a shorter sequence's end) has
-      // weight 0; guard -inf - -inf when every split so far is empty
+      // weight 0; guard -inf - -inf while every split so far is empty
       const float c = m == -INFINITY ? 0.0f : fast_exp2(m - mx);
       l *= c;
-      o *= c;
+      o.x *= c;
+      o.y *= c;
+      o.z *= c;
+      o.w *= c;
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const bool use = sp0 + u * P < n_split && mlv[u].x != -INFINITY;
         const float w = use ? fast_exp2(mlv[u].x - mx) : 0.0f;
         l = fmaf(mlv[u].y, w, l);
-        o = fmaf(aa[u], w, o);
+        o.x = fmaf(av[u].x, w, o.x);
+        o.y = fmaf(av[u].y, w, o.y);
+        o.z = fmaf(av[u].z, w, o.z);
+        o.w = fmaf(av[u].w, w, o.w);
       }
       m = mx;
     }
-    s.part[t] = m;
-    s.w[t] = l;
-    s.w[NT + t] = o;
+    s.m[t] = m;
+    s.l[t] = l;
+    s.o[t] = o;
     __syncthreads();
-    if (t < D) {
-      float M = s.part[t];
+    if (t < Q) {
+      float M = s.m[t];
 #pragma unroll
-      for (int p = 1; p < P; ++p) M = fmaxf(M, s.part[p * D + t]);
-      float L = 0.0f, O = 0.0f;
+      for (int p = 1; p < P; ++p) M = fmaxf(M, s.m[p * Q + t]);
+      float L = 0.0f;
+      float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const float mp = s.part[p * D + t];
+        const float mp = s.m[p * Q + t];
         const float w = mp == -INFINITY ? 0.0f : fast_exp2(mp - M);
-        L = fmaf(s.w[p * D + t], w, L);
-        O = fmaf(s.w[NT + p * D + t], w, O);
+        const float4 op = s.o[p * Q + t];
+        L = fmaf(s.l[p * Q + t], w, L);
+        O.x = fmaf(op.x, w, O.x);
+        O.y = fmaf(op.y, w, O.y);
+        O.z = fmaf(op.z, w, O.z);
+        O.w = fmaf(op.w, w, O.w);
       }
-      out[(int64_t)g * D + t] = (uint16_t)f2bf(O / L);
+      uint2 pk;
+      pk.x = pack_bf16x2(O.x / L, O.y / L);
+      pk.y = pack_bf16x2(O.z / L, O.w / L);
+      *reinterpret_cast<uint2*>(out + (int64_t)g * D + 4 * t) = pk;
     }
     __syncthreads();
   }
