@@ -14,11 +14,15 @@
 //   sum_t p_t v^_td = sum_t (p_t s_tg) c_td + sum_t p_t z_tg        (g = g(d))
 // Key codes enter the QK MFMA as bf16 128 + c (exact, one v_perm per pair);
 // the accumulator starts at -128 * sum_{d in g} q_d, which removes the offset.
-// Value codes enter the PV MFMA as exact fp16 c ((1024 + c) - 1024 with packed
-// fp16 subtracts; the matrix cores do not keep fp16 subnormal operands exact,
-// so c * 2^-24 bit patterns are not used), so the rounded p * s_V operand
-// (fp16, 11-bit significand) appears in no other term and needs no matching
-// correction. Q stays bf16 as given.
+// Value codes enter the PV MFMA as fp16 128 + c (exact: the code shifted into
+// the mantissa under a fixed high byte, no fp16 subtraction), against the A
+// operand a_t = fp16(p_t s_tg) (11-bit significand: the value and zero-point
+// terms of a short row cancel, so bf16 weights would be too coarse). One more
+// product of the same A operand against ones gives sum_t a_t per row, and 128
+// times it is subtracted at the end: the correction uses the very rounded a_t
+// the codes were multiplied by, so the offset cancels in fp32 (fp16 products
+// are exact there), at 128 / 7.5 times the accumulator's rounding of the bare
+// codes. Q stays bf16 as given.
 //
 // gfx950 design (v_mfma_f32_16x16x32_bf16 / _f16, one wave = 32 tokens per
 // tile, the next tile's loads in flight while the current one is computed):
@@ -30,7 +34,7 @@
 //     group g, so the accumulator column (h, g) collects the group-g partial
 //     dot; the groups are then summed with DPP and the scale/zero epilogue
 //     runs on every lane without padding waste;
-//   * PV (fp16 MFMA): A = p * s_V for the lane's (head, group) row and its 8
+//   * PV: A = p * s_V for the lane's (head, group) row and its 8
 //     tokens -- the very tokens and row the QK accumulator left in that lane,
 //     so no shuffle is needed -- and B = value codes, whose block layout makes
 //     a lane's operands for 4 consecutive 16-channel n-blocks one 16-byte load;
@@ -77,8 +81,8 @@ struct Int4DecodeArgs {
 };
 
 // 8 nibbles of a word -> 8 16-bit lanes whose low byte is the code and high
-// byte is HB (bf16 0x43.. = 128 + c, fp16 0x64.. = 1024 + c, both exact), in
-// the order low nibbles of bytes 0..3, then high nibbles.
+// byte is HB (bf16 0x43.. = 128 + c, exact), in the order low nibbles of
+// bytes 0..3, then high nibbles.
 template <uint32_t HB>
 __device__ __forceinline__ u32x4 nib8_to_16(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu;
@@ -94,14 +98,20 @@ __device__ __forceinline__ u32x4 nib8_to_16(uint32_t w) {
 __device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8, nib8_to_16<0x43u>(w));
 }
-// 8 nibbles -> exact fp16 codes c: (1024 + c) - 1024 with packed fp16 adds.
-__device__ __forceinline__ f16x8 nib8_to_f16(uint32_t w) {
-  const f16x8 biased = __builtin_bit_cast(f16x8, nib8_to_16<0x64u>(w));
-  const f16x8 off = {(_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f,
-                     (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f};
-  return biased - off;
+// 8 nibbles -> 8 fp16 values 128 + c (bits 0x5800 | c << 3, exact), same lane
+// order as nib8_to_16: the codes are moved to bits 3..6 of their bytes before
+// the high byte 0x58 is inserted.
+__device__ __forceinline__ f16x8 nib8_to_f16_128(uint32_t w) {
+  const uint32_t lo = (w << 3) & 0x78787878u;
+  const uint32_t hi = (w >> 1) & 0x78787878u;
+  const uint32_t cb = 0x58585858u;
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(cb, lo, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(cb, lo, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(cb, hi, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(cb, hi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
 }
-
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // (scale, zero) of a packed word as floats
 __device__ __forceinline__ float sz_scale(uint32_t w) {
@@ -298,6 +308,12 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
   f32x4 o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row sums of the PV A operand (p * s_V rounded to fp16), taken by one more
+  // product against ones: the value codes enter as 128 + c, so 128 times
+  // this sum is subtracted from every channel of the row at the end
+  f32x4 asum = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f16x8 ones8 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                       (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
   // FULL: all 32 tokens of the tile are below r1 (no masking, no stale
   // scale words); only the last tile of a split can be partial.
@@ -347,6 +363,7 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
         const float cr = __shfl(corr, ((4 * q4 + r) / NG) * NG, 64);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) o[nb][r] = scale_in_place(o[nb][r], cr);
+        asum[r] = scale_in_place(asum[r], cr);
       }
     }
     const float mq = m_run * qscale;
@@ -380,9 +397,9 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          pa, nib8_to_f16(word_of(T.v[nb / 4], nb % 4)), o[nb], 0, 0, 0);
+          pa, nib8_to_f16_128(word_of(T.v[nb / 4], nb % 4)), o[nb], 0, 0, 0);
+    asum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ones8, asum, 0, 0, 0);
   };
-
   // Ping-pong tiles: the next tile's loads are issued before the current tile
   // is computed. Tiles past the range are clamped to the last tile (a cached
   // re-read, never computed), so every load stays inside the allocation.
@@ -500,7 +517,8 @@ __global__ __launch_bounds__(64 * kI4Waves) void decode_int4_kernel(Int4DecodeAr
       const int row = 4 * q4 + r;
       const int h = row / NG, g = row % NG;
       if (row < NCOL && g == nb / 2)
-        red.acc[wave][h][16 * nb + n16] = wave_live ? o[nb][r] + zrow[r] : 0.0f;
+        red.acc[wave][h][16 * nb + n16] =
+            wave_live ? fmaf(-128.0f, asum[r], o[nb][r] + zrow[r]) : 0.0f;
     }
   }
   __syncthreads();
