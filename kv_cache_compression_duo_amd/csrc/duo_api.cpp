@@ -75,6 +75,18 @@ WsView ws_view(const duo_layer* L) {
   return v;
 }
 
+// Heads per block of the flash kernels for group size G (as their launcher
+// picks: 1 for G = 1, 2 for G = 2, 4 for G = 4 or 8).
+int heads_per_block(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
+
+// One partial sum per flash block of the gate gradient: 8 waves of 32 query
+// rows per block, heads_per_block heads sharing a block.
+size_t mixed_grad_partials(const duo_layer_desc& d, int T) {
+  const int G = d.n_q_heads / d.n_kv_heads, HB = heads_per_block(G);
+  const int BMT = 32 * 8 / HB;
+  return (size_t)d.batch * d.n_kv_heads * (G / HB) * (size_t)((T + BMT - 1) / BMT);
+}
+
 // true when the product of the factors stays at or below 2^62 bytes (no
 // buffer of a layer is larger; the bound also keeps every sum of such
 // products below 2^64)

@@ -1,6 +1,6 @@
 // Internal declarations shared by the C-ABI front end and the kernel launchers.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 #include "../../include/duo.h"
@@ -68,6 +68,7 @@ hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, c
                         const float* alpha, int T, int lam_block, void* out, hipStream_t s);
 // gate gradient of the gate-blended forward: partial sums per flash block
 // (mixed_grad_partials floats), then one reduction launch
+int heads_per_block(int G);
 size_t mixed_grad_partials(const duo_layer_desc& d, int T);
 hipError_t launch_mixed_alpha_grad(const duo_layer_desc& d, const void* q, const void* k,
                                    const void* v, const void* dout, const float* alpha,

@@ -699,15 +699,6 @@ __global__ __launch_bounds__(256) void alpha_grad_reduce_kernel(const float* __r
   }
 }
 
-// Heads per block of the flash kernels for group size G (as launch_d picks).
-static int heads_per_block(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
-
-size_t mixed_grad_partials(const duo_layer_desc& d, int T) {
-  const int G = d.n_q_heads / d.n_kv_heads, HB = heads_per_block(G);
-  const int BMT = 32 * 8 / HB;
-  return (size_t)d.batch * d.n_kv_heads * (G / HB) * (size_t)((T + BMT - 1) / BMT);
-}
-
 // Partials of the allocation-free gate gradient: one fp32 sum per flash block,
 // in a file-scope device array instead of a caller workspace. Every device the
 // library runs on holds its own copy until the process ends; every call on a
