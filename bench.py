@@ -99,43 +99,52 @@ def time_region(torch, fn, reps=1):
 
 
 # ---- measured HBM traffic (rocprofv3 counters) -------------------------------------
-# The decode kernel's HBM bytes per launch come from two rocprofv3 --pmc runs of
+# A decode kernel's HBM bytes per launch come from two rocprofv3 --pmc runs of
 # `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a device copy of known size in
 # the same run. `bench.py --traffic-summary FETCH_DIR WRITE_DIR` turns the two
-# runs into profiles/decode_kernel_llama2_7b_32k_traffic.json (+ .md). The
-# figure is reported only while the decode kernel's sources hash to the value
+# runs into one record per kernel under profiles/ (.json, read here, and .md).
+# A figure is reported only while the kernel's sources hash to the value
 # recorded with it.
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_32k_traffic.json")
-DECODE_SOURCES = ["k_decode.hip", "decode_common.hpp", "split_merge.hpp", "device_common.hpp",
-                  "duo_api.cpp", "duo_internal.hpp"]
+TRAFFIC = {
+    "decode": dict(
+        kernel="decode_kernel<128, 1, duo::Bf16Tag>", workload="llama2_7b_decode_32k",
+        json=os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_32k_traffic.json"),
+        sources=["k_decode.hip", "decode_common.hpp", "split_merge.hpp", "device_common.hpp",
+                 "duo_api.cpp", "duo_internal.hpp"]),
+    "int4": dict(
+        kernel="decode_int4_kernel<128, 4, duo::Fp16Tag>", workload="llama3_8b_int4_decode_1m",
+        json=os.path.join(ROOT, "profiles", "decode_int4_kernel_llama3_8b_1m_traffic.json"),
+        sources=["k_decode_int4.hip", "int4_codec.hpp", "decode_common.hpp", "split_merge.hpp",
+                 "device_common.hpp", "duo_api.cpp", "duo_internal.hpp"]),
+}
 COPY_BYTES = 256 << 20
-DECODE_KERNEL = "decode_kernel<128, 1, duo::Bf16Tag>"
 
 
-def decode_source_hash() -> str:
+def source_hash(key: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in TRAFFIC[key]["sources"]:
         with open(os.path.join(ROOT, "kv_cache_compression_duo_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(key: str = "decode"):
     try:
-        with open(TRAFFIC_JSON) as fh:
+        with open(TRAFFIC[key]["json"]) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != decode_source_hash():
+    if t.get("source_hash") != source_hash(key):
         return None  # the kernel changed since the counters were taken
     return t.get("bytes_per_launch")
 
 
 def traffic_probe(dev):
     """Launches profiled by the two counter runs: decode steps of one layer of
-    the headline workload, then a plain device copy of COPY_BYTES."""
+    the Llama-2 workload, decode steps of the 1M-token 4-bit layer, then a
+    plain device copy of COPY_BYTES."""
     import torch
     import kv_cache_compression_duo_amd as duo
     from duo_synth import WORKLOADS, device_normal
@@ -154,56 +163,129 @@ def traffic_probe(dev):
     out = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
     for s in range(steps):
         lay.decode(q[s], kn[s], vn[s], out)
+    del lay
+    w4 = WORKLOADS["llama3_8b_int4_decode_1m"]
+    Hq, Hkv, D, Hr = w4.n_q_heads, w4.n_kv_heads, w4.head_dim, w4.n_retrieval_kv
+    steps4 = 4
+    lay4 = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
+                        capacity=w4.context + steps4, softmax_scale=w4.softmax_scale,
+                        kv_dtype="fp16", retrieval_dtype="int4", device=dev)
+    for a in range(0, w4.context, 65536):
+        lay4.append_kv(device_normal((1, 65536, Hkv, D), 5000 + a // 65536, dev, torch.float16),
+                       device_normal((1, 65536, Hkv, D), 6000 + a // 65536, dev, torch.float16))
+    q4 = device_normal((steps4, 1, 1, Hq, D), 51, dev, torch.bfloat16)
+    kn4 = device_normal((steps4, 1, 1, Hkv, D), 52, dev, torch.float16)
+    vn4 = device_normal((steps4, 1, 1, Hkv, D), 53, dev, torch.float16)
+    out4 = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    for s in range(steps4):
+        lay4.decode(q4[s], kn4[s], vn4[s], out4)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"# traffic probe: {steps} decode launches, 3 copies of {COPY_BYTES} bytes",
+    print(f"# traffic probe: {steps} + {steps4} decode launches, 3 copies of {COPY_BYTES} bytes",
           file=sys.stderr, flush=True)
 
 
-def _pmc_means(run_dir, counter):
-    """Mean counter value per dispatch, by kernel name, from a rocprofv3 csv run."""
+def _csv_rows(run_dir, suffix):
     import csv
     import glob
-    vals = {}
-    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+    for f in sorted(glob.glob(os.path.join(run_dir, "**", "*" + suffix), recursive=True)):
         with open(f, newline="") as fh:
-            for row in csv.DictReader(fh):
-                if row.get("Counter_Name") != counter:
-                    continue
-                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+            yield from csv.DictReader(fh)
+
+
+def _pmc_values(run_dir, counter):
+    """Counter values per dispatch, by kernel name, from a rocprofv3 csv run."""
+    vals = {}
+    for row in _csv_rows(run_dir, "counter_collection.csv"):
+        if row.get("Counter_Name") == counter:
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def _pmc_means(run_dir, counter):
+    return {k: sum(v) / len(v) for k, v in _pmc_values(run_dir, counter).items()}
 
 
 def traffic_summary(fetch_dir, write_dir):
     fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
     write = _pmc_means(write_dir, "WRITE_SIZE")
+
     def pick(d, key):
         names = [k for k in d if key in k]
         if len(names) != 1:
             raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
         return names[0], d[names[0]]
-    dec_name, f_dec = pick(fetch, DECODE_KERNEL)
-    _, w_dec = pick(write, DECODE_KERNEL)
     copy_name, f_copy = pick(fetch, "__amd_rocclr_copyBuffer")
     _, w_copy = pick(write, "__amd_rocclr_copyBuffer")
     kib = COPY_BYTES / 1024.0
     f_scale, w_scale = kib / f_copy, kib / w_copy
-    fetch_b = f_dec * f_scale * 1024.0
-    write_b = w_dec * w_scale * 1024.0
-    t = {"kernel": dec_name, "workload": "llama2_7b_decode_32k",
-         "fetch_kib_per_launch": f_dec, "write_kib_per_launch": w_dec,
-         "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
-         "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
-         "fetch_scale": f_scale, "write_scale": w_scale,
-         "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
-         "bytes_per_launch": fetch_b + write_b, "source_hash": decode_source_hash()}
-    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
-    with open(TRAFFIC_JSON, "w") as fh:
-        json.dump(t, fh, indent=1)
-    print(json.dumps(t, indent=1))
+    for key, spec in TRAFFIC.items():
+        name, f_k = pick(fetch, spec["kernel"])
+        _, w_k = pick(write, spec["kernel"])
+        fetch_b = f_k * f_scale * 1024.0
+        write_b = w_k * w_scale * 1024.0
+        t = {"kernel": name, "workload": spec["workload"],
+             "fetch_kib_per_launch": f_k, "write_kib_per_launch": w_k,
+             "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
+             "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+             "fetch_scale": f_scale, "write_scale": w_scale,
+             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+             "bytes_per_launch": fetch_b + write_b, "source_hash": source_hash(key)}
+        os.makedirs(os.path.dirname(spec["json"]), exist_ok=True)
+        with open(spec["json"], "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t, indent=1))
+
+
+def kernel_summary(trace_dir, group=8):
+    """Markdown table of the library's kernels in a rocprofv3 --kernel-trace
+    csv run: calls and durations, and for the flash kernels the totals of
+    consecutive groups of `group` dispatches (one per prefill pass of 8
+    chunks), in dispatch order."""
+    per = {}
+    for row in _csv_rows(trace_dir, "kernel_trace.csv"):
+        name = row["Kernel_Name"]
+        if "duo::" not in name:
+            continue
+        t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+        per.setdefault(name, []).append((t0, (t1 - t0) / 1000.0))
+    print("| kernel | calls | average us | min us | max us | total ms |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = [x for _, x in sorted(v)]
+        print(f"| `{name}` | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} "
+              f"| {sum(d) / 1000:.3f} |")
+    print()
+    for name, v in sorted(per.items()):
+        if "attn_kernel<128, 4, 0>" not in name and "attn_kernel<128, 4, 1>" not in name:
+            continue
+        d = [x for _, x in sorted(v)]
+        passes = [sum(d[i:i + group]) / 1000 for i in range(0, len(d) - group + 1, group)]
+        print(f"`{name}`: totals of successive groups of {group} dispatches (ms): "
+              + ", ".join(f"{x:.3f}" for x in passes))
+
+
+def counter_summary(*run_dirs):
+    """Per-dispatch averages of every counter in rocprofv3 --pmc csv runs, by
+    kernel, with the dispatch duration where the run records it."""
+    rows = {}
+    for rd in run_dirs:
+        for row in _csv_rows(rd, "counter_collection.csv"):
+            name = row["Kernel_Name"]
+            if "duo::" not in name:
+                continue
+            rows.setdefault(name, {}).setdefault(row["Counter_Name"], []).append(
+                float(row["Counter_Value"]))
+            if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                rows[name].setdefault("_duration_us@" + rd, []).append(
+                    (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
+    out = {}
+    for name, cs in rows.items():
+        out[name] = {c: sum(v) / len(v) for c, v in cs.items()}
+    print(json.dumps(out, indent=1))
 
 
 # ---- workloads -------------------------------------------------------------------
@@ -258,7 +340,7 @@ def bench_decode_llama2(args, dev):
         "value": gbs, "ms_per_step": ms_step, "tok_per_s": 1000.0 / ms_step,
         "bytes_per_step": nbytes / args.steps, "layers_cycled": L,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                      "kernel": "duo::decode_kernel<128, 1, duo::Bf16Tag>",
                      "avg_launch_us": ms_step * 1e3},
     }
@@ -463,7 +545,9 @@ def bench_int4_decode(args, dev):
     ms = t0.elapsed_time(t1)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms_per_step": ms / steps, "tok_per_s": 1000.0 * steps / ms, "kv_gbs": gbs,
-            "bytes_per_step": nbytes / steps, "hbm_frac": gbs / HBM_PEAK_GBS}
+            "bytes_per_step": nbytes / steps, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "traffic": measured_traffic("int4"),
+            "kernel": "duo::decode_int4_kernel<128, 4, duo::Fp16Tag>"}
 
 
 def cpu_model() -> str:
@@ -540,10 +624,20 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the counter runs measure")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 csv runs into the traffic record")
+                    help="summarise two rocprofv3 csv runs into the traffic records")
+    ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
+                    help="markdown table of a rocprofv3 --kernel-trace csv run")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR",
+                    help="per-kernel counter averages of rocprofv3 --pmc csv runs")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.kernel_summary:
+        kernel_summary(args.kernel_summary)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build",
