@@ -19,8 +19,7 @@
 // gfx950 design:
 //   * a block is 8 waves; a wave owns 32 query rows (32 tokens of one query
 //     head). The HB heads of a block share one KV head (GQA grouping), so one
-//     K/V tile in LDS serves 8 waves of query rows; half the waves stage K and
-//     half V;
+//     K/V tile in LDS serves 8 waves of query rows;
 //   * the mixed forward runs in two phases over one tile pipeline and one
 //     softmax state: the Lambda tiles (sinks and the window band, a few per
 //     query tile) first, folded into (1 - alpha) * O / l kept as bf16 pairs,
@@ -31,12 +30,18 @@
 //     cross-lane exchange per tile, and the score accumulator is directly the
 //     B operand of the PV product (keys permuted inside each 16-key slice,
 //     which a sum over keys does not see);
-//   * K tiles are stored row-major in LDS (rows padded by 16 bytes), V tiles
-//     transposed (d-major) with 4-key chunks paired and XOR-swizzled by d, so
-//     that both MFMA operands are read with one ds_read_b128 each;
-//   * the next tile's global loads are in flight while the current tile is
+//   * K and V tiles go from global memory straight into LDS (16-byte buffer
+//     loads with the LDS bit: no VGPRs, no repacking VALU, no ds_write), all
+//     8 waves issuing a share. Both are stored row-major with 16-byte chunks
+//     XOR-swizzled by row. K fragments are one ds_read_b128 each; V^T
+//     fragments are two transposed reads (ds_read_b64_tr_b16) each, so V
+//     needs no transposing copy. Streaming mode, which gathers rows from the
+//     ring and the chunk per lane, stages through registers instead (K rows
+//     padded by 16 bytes, V transposed on the way to LDS);
+//   * the next tile's loads are in flight while the current tile is
 //     computed; query tiles are launched longest-first (causal imbalance).
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "duo_internal.hpp"
@@ -83,6 +88,27 @@ constexpr int kBN = 64;  // keys per tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const void* p) {
+  return (__attribute__((address_space(3))) void*)(const_cast<void*>(p));
+}
+
+// Two transposed 8-byte LDS reads (ds_read_b64_tr_b16) joined into one MFMA
+// operand. In each group of 16 lanes, lane i receives element i % 4 of the
+// 4-element chunks read by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4:
+// when lane c reads row c / 4 (of four consecutive rows) at columns
+// 4 (c % 4) .. 4 (c % 4) + 3 of a 16-column strip, lane i gets column i of
+// the four rows.
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* lo, const char* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(lo)));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(hi)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Position (in 8-byte units) of the 4-key chunk c of V^T row d in LDS. Chunks
@@ -148,10 +174,20 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // the gate-blended forward and its gate gradient visit the Lambda tiles,
   // then all causal tiles
   constexpr bool kTwoPhase = kMixed || kGrad;
+  // Modes that read K and V through one buffer resource each stage them
+  // with direct global->LDS loads (see below); streaming mode gathers rows
+  // per lane through registers.
+  constexpr bool kDma = MODE != MODE_STREAMING;
+  constexpr int KROW = kDma ? D : KPAD;  // K tile row stride in LDS (elements)
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
-  // written to the other, so one barrier per tile suffices
-  __shared__ __align__(16) uint16_t Ks[2][kBN * KPAD];
-  __shared__ __align__(16) uint16_t Vt[2][D * kBN];
+  // written to the other, so one barrier per tile suffices. The stages are
+  // separate arrays, each named statically in the (twice unrolled) loop, so
+  // the compiler sees that reads of one stage do not wait for the direct
+  // loads into the other.
+  __shared__ __align__(16) uint16_t Ks0[kBN * KROW];
+  __shared__ __align__(16) uint16_t Ks1[kBN * KROW];
+  __shared__ __align__(16) uint16_t Vs0[D * kBN];
+  __shared__ __align__(16) uint16_t Vs1[D * kBN];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -212,32 +248,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qp + 16 * ks));
   }
 
-  // ---- global -> register staging of one K/V tile ------------------------------
-  // 256 threads stage K and 256 stage V; the roles are wave-uniform.
-  // Retrieval mode (the head's cached rows) and the mixed forward (the
-  // sequence's rows of one KV head, a row stride of Hkv*D) read K and V each
-  // as one buffer resource. Rows at or past the last key read as zeros (the
-  // causal mask removes them), a tile's addresses are one add per lane (53
-  // fewer VALU per tile than per-row pointers), and both roles load into one
-  // set of registers (the 128-bit buffer loads keep their width; with plain
-  // pointers a shared set made the compiler split them into 4-byte loads).
-  // Streaming mode gathers rows per lane from the ring and the chunk and
-  // keeps a set per role.
+  // ---- staging of one K/V tile ---------------------------------------------------
   static_assert(NW == 8, "the staging roles assume 8 waves");
-  constexpr bool kBuf = MODE != MODE_STREAMING;
-  const int st_t = tid & 255;
-  const bool stage_k = wave >= 4;
-  const int kr_row = st_t >> 2, kr_d0 = (st_t & 3) * (D / 4);
-  const int vg = st_t & 15, vdc = st_t >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
-  const bool v_active = !stage_k && vdc < D / 8;
-  u32x4 kreg[4];                    // K: KLD chunks of a row (and V when kBuf)
-  u32x4 vown[kBuf ? 1 : 4];         // V: one d-chunk of 4 keys
-  auto vreg = [&](int r) -> u32x4& {
-    if constexpr (kBuf) return kreg[r];
-    else return vown[r];
-  };
-  // buffer view: row stride, first element and readable bytes (the host
-  // keeps every such range below 2^31 bytes)
+  // Buffer view of K and V: row stride, first element and readable bytes
+  // (the host keeps every such range below 2^31 bytes). Retrieval mode reads
+  // the head's cached rows, the mixed forward the sequence's rows of one KV
+  // head (a row stride of Hkv*D).
   const uint32_t rstride = (uint32_t)(MODE == MODE_RETRIEVAL ? D * 2 : a.Hkv * D * 2);
   const int64_t hoff = MODE == MODE_RETRIEVAL ? ((int64_t)b * a.Hr + kv) * a.cap * D
                                               : ((int64_t)b * a.T * a.Hkv + kv) * D;
@@ -245,46 +261,86 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       MODE == MODE_RETRIEVAL ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2)
                              : (uint32_t)((int64_t)a.T * a.Hkv - kv) * (uint32_t)(D * 2);
   const __amdgpu_buffer_rsrc_t krs =
-      wave_rsrc((MODE == MODE_RETRIEVAL ? a.kc : a.k_in) + (kBuf ? hoff : 0), kBuf ? rbytes : 0u);
+      wave_rsrc((MODE == MODE_RETRIEVAL ? a.kc : a.k_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
   const __amdgpu_buffer_rsrc_t vrs =
-      wave_rsrc((MODE == MODE_RETRIEVAL ? a.vc : a.v_in) + (kBuf ? hoff : 0), kBuf ? rbytes : 0u);
-  const uint32_t k_voff = (uint32_t)kr_row * rstride + (uint32_t)kr_d0 * 2u;
-  const uint32_t v_voff = (uint32_t)(4 * vg) * rstride + (uint32_t)(8 * vdc) * 2u;
-  auto load_k = [&](int p0) {
-    if constexpr (kBuf) {
-      const uint32_t o = k_voff + (uint32_t)p0 * rstride;
+      wave_rsrc((MODE == MODE_RETRIEVAL ? a.vc : a.v_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
+
+  // Direct loads (kDma). A 16-byte buffer load with the LDS bit writes lane
+  // i's data to the instruction's LDS base + 16 i, so a 1 KB block of a tile
+  // is filled by giving each lane the source chunk that belongs in its slot.
+  // Rows are 2D bytes, unpadded, with 16-byte chunks XOR-swizzled by row so
+  // that the MFMA operand reads below spread over the LDS banks:
+  //   K: chunk c of row r sits in slot c ^ ksw(r), ksw(r) = r & 15 for
+  //      256-byte rows and (r >> 1) & 7 for 128-byte rows: the 16 rows that
+  //      16 lanes read together take 16 distinct slots of a 256-byte window;
+  //   V: 32-byte segment g of row r sits in segment g ^ vsw(r), vsw(r) =
+  //      2 (r & 3) for 256-byte rows and r & 3 for 128-byte rows: a
+  //      transposed read takes 4 consecutive rows x 2 adjacent segments per
+  //      32 lanes, 8 distinct segments.
+  // Each wave issues D/64 loads of K and D/64 of V per tile. Rows past the
+  // last key are clamped to it: the mask removes them, their values only
+  // have to be finite. Neither the data nor its repacking passes through
+  // VGPRs.
+  constexpr int RB = 2 * D;       // bytes per LDS row (direct layout)
+  constexpr int SPR = RB / 16;    // 16-byte slots per row
+  constexpr int RPI = 64 / SPR;   // rows per 1 KB load
+  constexpr int NIW = D / 64;     // loads per wave per tensor and tile
+  auto ksw = [](int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
+  auto vsw = [](int r) { return RB == 256 ? 2 * (r & 3) : (r & 3); };
+  const int last_row = (MODE == MODE_RETRIEVAL ? a.n + a.T : a.T) - 1;
+  const int dma_row0 = wave * NIW * RPI + lane / SPR;  // this lane's row in the wave's first block
+  uint32_t k_c16[NIW], v_c16[NIW];  // byte offset of the chunk a lane fetches within its row
 #pragma unroll
-      for (int c = 0; c < KLD; ++c) kreg[c] = buf_ld16(krs, o + 16 * c, 0);
-    } else {
-      const uint16_t* kp = stream_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
+  for (int j = 0; j < NIW; ++j) {
+    const int r = dma_row0 + j * RPI, pos = lane % SPR;
+    k_c16[j] = (uint32_t)(pos ^ ksw(r)) * 16u;
+    v_c16[j] = (uint32_t)(2 * ((pos >> 1) ^ vsw(r)) + (pos & 1)) * 16u;
+  }
+  auto dma_tile = [&](int p0, uint16_t* ks, uint16_t* vs) {
 #pragma unroll
-      for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
+    for (int j = 0; j < NIW; ++j) {
+      const int blk = wave * NIW + j;  // the wave's j-th 1 KB block of the tile
+      int r = p0 + dma_row0 + j * RPI;
+      r = r < last_row ? r : last_row;
+      const uint32_t ro = (uint32_t)r * rstride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(ks + blk * 512), 16, (int)(ro + k_c16[j]),
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds_ptr(vs + blk * 512), 16, (int)(ro + v_c16[j]),
+                                               0, 0, 0);
     }
+  };
+
+  // Register staging (streaming mode): 256 threads gather K rows and 256
+  // threads V rows per lane from the ring and the chunk; V is transposed
+  // into d-major rows (vt_slot) on the way to LDS.
+  const int st_t = tid & 255;
+  const bool stage_k = wave >= 4;
+  const int kr_row = st_t >> 2, kr_d0 = (st_t & 3) * (D / 4);
+  const int vg = st_t & 15, vdc = st_t >> 4;  // V: keys 4vg..4vg+3, d-chunk 8*vdc
+  const bool v_active = !stage_k && vdc < D / 8;
+  u32x4 kreg[4];  // K: KLD chunks of a row (unused, and removed, in the direct modes)
+  u32x4 vown[4];  // V: one d-chunk of 4 keys
+  auto load_k = [&](int p0) {
+    const uint16_t* kp = stream_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
+#pragma unroll
+    for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
   };
   auto load_v = [&](int p0) {
-    if constexpr (kBuf) {
-      const uint32_t o = v_voff + (uint32_t)p0 * rstride;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vreg(r) = buf_ld16(vrs, o + (uint32_t)r * rstride, 0);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg(r) = ld16(stream_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
-    }
+    for (int r = 0; r < 4; ++r)
+      vown[r] = ld16(stream_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
   };
-  auto store_k = [&](int stage) {
-    uint16_t* ks = Ks[stage];
+  auto store_k = [&](uint16_t* ks) {
 #pragma unroll
     for (int c = 0; c < KLD; ++c) st16(ks + kr_row * KPAD + kr_d0 + 8 * c, kreg[c]);
   };
-  auto store_v = [&](int stage) {
-    uint16_t* vt = Vt[stage];
+  auto store_v = [&](uint16_t* vt) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int d = 8 * vdc + i;
       const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t lo = __builtin_amdgcn_perm(word_of(vreg(1), i >> 1), word_of(vreg(0), i >> 1), sel);
-      uint32_t hi = __builtin_amdgcn_perm(word_of(vreg(3), i >> 1), word_of(vreg(2), i >> 1), sel);
+      uint32_t lo = __builtin_amdgcn_perm(word_of(vown[1], i >> 1), word_of(vown[0], i >> 1), sel);
+      uint32_t hi = __builtin_amdgcn_perm(word_of(vown[3], i >> 1), word_of(vown[2], i >> 1), sel);
       uint32_t* dst = reinterpret_cast<uint32_t*>(vt + d * kBN + 4 * vt_slot(vg, d));
       dst[0] = lo;
       dst[1] = hi;
@@ -294,9 +350,9 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     if (stage_k) load_k(p0);
     if (v_active) load_v(p0);
   };
-  auto store_tile = [&](int stage) {
-    if (stage_k) store_k(stage);
-    if (v_active) store_v(stage);
+  auto store_tile = [&](uint16_t* ks, uint16_t* vt) {
+    if (stage_k) store_k(ks);
+    if (v_active) store_v(vt);
   };
 
   // ---- state --------------------------------------------------------------------
@@ -386,6 +442,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       }
     l += ls0 + ls1;
   };
+  // V^T fragment of lane (q32, h2) for slice s and d-block db: channel
+  // 32 db + q32 of keys 16s + 4 h2 .. + 3 and 16s + 8 + 4 h2 .. + 3. In the
+  // direct layout (V rows in LDS) it takes two transposed reads: the 16-lane
+  // group (h2, dsub = bit 4 of the lane) reads rows 4 h2 + c / 4 (plus the
+  // slice's first key, plus 8 for the second half) at channels
+  // 32 db + 16 dsub + 4 (c % 4), c = lane % 16; v_lane is that address for
+  // db = 0 and the slice's first key, the segment of block db being an XOR.
+  const int c16 = lane & 15, dsub = (lane >> 4) & 1;
+  const uint32_t v_lane = (uint32_t)((4 * h2 + (c16 >> 2)) * RB + ((dsub ^ vsw(c16 >> 2)) << 5) +
+                                     ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8);
   auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
     // all V^T fragments of two 16-key slices are requested before their
     // products (the empty asm keeps the compiler from sinking each read next
@@ -397,10 +463,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
-          const int d = 32 * db + q32;
-          av[h][db] = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(vt + d * kBN + 4 * vt_slot(4 * (s2 + h) + h2, d)));
+          if constexpr (kDma) {
+            const char* p = reinterpret_cast<const char*>(vt) + (v_lane ^ (uint32_t)(db << 6)) +
+                            16 * (s2 + h) * RB;
+            av[h][db] = lds_tr_pair(p, p + 8 * RB);
+          } else {
+            // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
+            const int d = 32 * db + q32;
+            av[h][db] = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(vt + d * kBN + 4 * vt_slot(4 * (s2 + h) + h2, d)));
+          }
         }
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -415,20 +487,37 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // K fragments of a block are requested before its first product (as for V
   // above), and the two blocks' independent accumulation chains are
   // interleaved.
+  // K fragment of lane (q32, h2) for k-step ks_: chunk 2 ks_ + h2 of key rows
+  // q32 and q32 + 32; in the direct layout at slot (2 ks_ + h2) ^ ksw(q32)
+  // (ksw(q32 + 32) = ksw(q32)), an XOR of k_lane by 32 ks_.
+  const uint32_t k_lane = (uint32_t)(q32 * RB + ((h2 ^ ksw(q32)) << 4));
   auto qk = [&](const uint16_t* ks, f32x16 (&st)[2]) {
     st[0] = f32x16{};
     st[1] = f32x16{};
-    const uint16_t* krow0 = ks + q32 * KPAD + 8 * h2;
-    const uint16_t* krow1 = krow0 + 32 * KPAD;
     bf16x8 ak0[KS], ak1[KS];
+    if constexpr (kDma) {
+      const char* kb = reinterpret_cast<const char*>(ks);
 #pragma unroll
-    for (int ks_ = 0; ks_ < KS; ++ks_)
-      ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks_));
-    asm volatile("" ::: "memory");
+      for (int ks_ = 0; ks_ < KS; ++ks_)
+        ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5))));
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int ks_ = 0; ks_ < KS; ++ks_)
-      ak1[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks_));
-    asm volatile("" ::: "memory");
+      for (int ks_ = 0; ks_ < KS; ++ks_)
+        ak1[ks_] = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5)) + 32 * RB));
+      asm volatile("" ::: "memory");
+    } else {
+      const uint16_t* krow0 = ks + q32 * KPAD + 8 * h2;
+      const uint16_t* krow1 = krow0 + 32 * KPAD;
+#pragma unroll
+      for (int ks_ = 0; ks_ < KS; ++ks_)
+        ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks_));
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int ks_ = 0; ks_ < KS; ++ks_)
+        ak1[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks_));
+      asm volatile("" ::: "memory");
+    }
 #pragma unroll
     for (int ks_ = 0; ks_ < KS; ++ks_) {
       st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks_], qf[ks_], st[0], 0, 0, 0);
@@ -490,8 +579,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 
   // ---- main loop ----------------------------------------------------------------
   {
-    load_tile(tile_pos(0));
-    store_tile(0);
+    if constexpr (kDma) {
+      dma_tile(tile_pos(0), Ks0, Vs0);
+    } else {
+      load_tile(tile_pos(0));
+      store_tile(Ks0, Vs0);
+    }
     __syncthreads();
     // Every load issued so far (the query fragments, tile 0) has landed: say
     // so explicitly. Without it the wait-count insertion merges the path on
@@ -500,10 +593,21 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     // next tile's prefetch (vmcnt counts in order), exposing its whole
     // latency.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    for (int k = 0; k < ntiles; ++k) {
-      const int stage = k & 1;
+    // One tile from stage S (0 or 1, a compile-time constant): the next
+    // tile's loads go to the other stage, which was last read before the
+    // previous barrier. Direct loads complete before the barrier that ends
+    // the step (the barrier waits for the wave's outstanding loads).
+    auto step = [&](int k, auto stage) {
+      constexpr int S = decltype(stage)::value;
+      uint16_t* ks = S ? Ks1 : Ks0;
+      uint16_t* vs = S ? Vs1 : Vs0;
+      uint16_t* ks_next = S ? Ks0 : Ks1;
+      uint16_t* vs_next = S ? Vs0 : Vs1;
       const bool more = k + 1 < ntiles;
-      if (more) load_tile(tile_pos(k + 1));
+      if (more) {
+        if constexpr (kDma) dma_tile(tile_pos(k + 1), ks_next, vs_next);
+        else load_tile(tile_pos(k + 1));
+      }
       if (kTwoPhase && k == nlam) {
         // end of the Lambda phase: keep (1 - alpha) * O / l (forward) or
         // dout . O / l (gate gradient), restart the state
@@ -524,11 +628,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
         l_f = 0.0f;
       }
       f32x16 st[2];
-      qk(Ks[stage], st);
-      consume(k, st, Vt[stage]);
-      // the other stage was last read before the previous barrier
-      if (more) store_tile(stage ^ 1);
+      qk(ks, st);
+      consume(k, st, vs);
+      if constexpr (!kDma) {
+        if (more) store_tile(ks_next, vs_next);
+      }
       __syncthreads();
+    };
+    for (int k = 0; k < ntiles; k += 2) {
+      step(k, std::integral_constant<int, 0>());
+      if (k + 1 < ntiles) step(k + 1, std::integral_constant<int, 1>());
     }
   }
 
