@@ -296,16 +296,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     k_c16[j] = (uint32_t)(pos ^ ksw(r)) * 16u;
     v_c16[j] = (uint32_t)(2 * ((pos >> 1) ^ vsw(r)) + (pos & 1)) * 16u;
   }
-  auto dma_tile = [&](int p0, uint16_t* ks, uint16_t* vs) {
+  // the rows p0 .. p0 + 63 of one tensor into the stage at dst
+  auto dma_rows = [&](int p0, uint16_t* dst, __amdgpu_buffer_rsrc_t rs,
+                      const uint32_t (&c16)[NIW]) {
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
       const int blk = wave * NIW + j;  // the wave's j-th 1 KB block of the tile
       int r = p0 + dma_row0 + j * RPI;
       r = r < last_row ? r : last_row;
       const uint32_t ro = (uint32_t)r * rstride;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(ks + blk * 512), 16, (int)(ro + k_c16[j]),
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds_ptr(vs + blk * 512), 16, (int)(ro + v_c16[j]),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + blk * 512), 16, (int)(ro + c16[j]),
                                                0, 0, 0);
     }
   };
@@ -400,8 +400,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // B operands of the four 16-key slices.
   const float c2 = a.scale_log2;
   const float lazy = 8.0f / c2;  // raw-score growth that forces a rescale
-  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB],
-                            bf16x8 (&pb)[4]) {
+  auto softmax_rescale = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB]) {
     float tm = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -419,6 +418,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int db = 0; db < DB; ++db) O[db] *= corr;
       m = mn;
     }
+  };
+  auto softmax_weights = [&](const f32x16 (&sc)[2], float m, float& l, bf16x8 (&pb)[4]) {
     const float mc = m == -INFINITY ? 0.0f : m * c2;  // no allowed key yet: p = 0
     float p[2][16];
 #pragma unroll
@@ -441,6 +442,11 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
                                               false);
       }
     l += ls0 + ls1;
+  };
+  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB],
+                            bf16x8 (&pb)[4]) {
+    softmax_rescale(sc, m, l, O);
+    softmax_weights(sc, m, l, pb);
   };
   // V^T fragment of lane (q32, h2) for slice s and d-block db: channel
   // 32 db + q32 of keys 16s + 4 h2 .. + 3 and 16s + 8 + 4 h2 .. + 3. In the
@@ -524,63 +530,87 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks_], qf[ks_], st[1], 0, 0, 0);
     }
   };
-  // Masked scores, softmax update and PV product of tile k from its raw
-  // scores st and V tile vt. Tiles wholly below the wave's first query need
-  // no causal mask, tiles wholly above its last query are skipped.
-  auto consume = [&](int k, f32x16 (&st)[2], const uint16_t* vt) {
+  // Causal / Lambda mask of tile k's raw scores, in place (unmasked tiles
+  // use the product registers as they are: a separate masked copy cost 32
+  // moves per tile on the unmasked path). Tiles wholly below the wave's
+  // first query need none.
+  auto mask_scores = [&](int k, f32x16 (&st)[2]) {
     const int p0 = tile_pos(k);
     const bool lam_phase = MODE == MODE_STREAMING || (kTwoPhase && k < nlam);
-    const bool live = p0 <= i_wlast;
     const bool diag = p0 + kBN - 1 > i_wfirst;
-    if (live) {
-      // masked in place: unmasked tiles use the product registers as they are
-      // (a separate masked copy cost 32 moves per tile on the unmasked path)
-      if (lam_phase || diag) {
-        // Element j of the lane's scores is key base + c_j, with c_j a
-        // compile-time offset. One loop per mode (a tile-uniform branch
-        // between two loops made the compiler copy the scores at the join
-        // on every tile). Bitwise operators: a select per element, no
-        // per-lane branches.
-        const int base = p0 + 4 * h2;
-        if constexpr (MODE == MODE_RETRIEVAL || lblk) {
-          // causal: c_j <= dq; under the block mask a 64-key tile is one
-          // block, visible to a query or not as a whole
-          int dq = i_q - base;
-          if constexpr (lblk) {
-            const bool vis = ((p0 >> 6) < sbk) | (((i_q >> 6) - (p0 >> 6)) < rbk);
-            dq = (lam_phase & !vis) ? -1 : dq;
-          }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
-              st[kb][j] = c <= dq ? st[kb][j] : -INFINITY;
-            }
-        } else {
-          // token-level Lambda; outside the Lambda phase every key passes
-          // the sink test, leaving the causal one
-          const int s_lim = lam_phase ? a.S : 0x7fffffff;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int jp = base + 32 * kb + 8 * (j >> 2) + (j & 3);
-              const bool ok = (jp <= i_q) & ((jp < s_lim) | (i_q - jp < a.R));
-              st[kb][j] = ok ? st[kb][j] : -INFINITY;
-            }
+    if (lam_phase || diag) {
+      // Element j of the lane's scores is key base + c_j, with c_j a
+      // compile-time offset. One loop per mode (a tile-uniform branch
+      // between two loops made the compiler copy the scores at the join on
+      // every tile). Bitwise operators: a select per element, no per-lane
+      // branches.
+      const int base = p0 + 4 * h2;
+      if constexpr (MODE == MODE_RETRIEVAL || lblk) {
+        // causal: c_j <= dq; under the block mask a 64-key tile is one
+        // block, visible to a query or not as a whole
+        int dq = i_q - base;
+        if constexpr (lblk) {
+          const bool vis = ((p0 >> 6) < sbk) | (((i_q >> 6) - (p0 >> 6)) < rbk);
+          dq = (lam_phase & !vis) ? -1 : dq;
         }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
+            st[kb][j] = c <= dq ? st[kb][j] : -INFINITY;
+          }
+      } else {
+        // token-level Lambda; outside the Lambda phase every key passes the
+        // sink test, leaving the causal one
+        const int s_lim = lam_phase ? a.S : 0x7fffffff;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int jp = base + 32 * kb + 8 * (j >> 2) + (j & 3);
+            const bool ok = (jp <= i_q) & ((jp < s_lim) | (i_q - jp < a.R));
+            st[kb][j] = ok ? st[kb][j] : -INFINITY;
+          }
       }
+    }
+  };
+  // Masked scores, softmax update and PV product of tile k from its raw
+  // scores st and V tile vt; tiles wholly above the wave's last query are
+  // skipped.
+  auto consume = [&](int k, f32x16 (&st)[2], const uint16_t* vt) {
+    if (tile_pos(k) <= i_wlast) {
+      mask_scores(k, st);
       bf16x8 pb[4];
       softmax_update(st, m_f, l_f, o_f, pb);
       pv(vt, pb, o_f);
     }
   };
+  // End of the Lambda phase of the two-phase modes: keep (1 - alpha) * O / l
+  // (forward) or dout . O / l (gate gradient), restart the state.
+  auto end_lambda_phase = [&]() {
+    const float ll = l_f + __shfl_xor(l_f, 32, 64);
+    if constexpr (kGrad) {
+      g_lam = dout_dot(1.0f / ll);
+    } else {
+      const float wl = (1.0f - alpha) / ll;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
+    m_f = -INFINITY;
+    l_f = 0.0f;
+  };
 
   // ---- main loop ----------------------------------------------------------------
   {
     if constexpr (kDma) {
-      dma_tile(tile_pos(0), Ks0, Vs0);
+      dma_rows(tile_pos(0), Ks0, krs, k_c16);
+      dma_rows(tile_pos(0), Vs0, vrs, v_c16);
     } else {
       load_tile(tile_pos(0));
       store_tile(Ks0, Vs0);
@@ -593,7 +623,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     // next tile's prefetch (vmcnt counts in order), exposing its whole
     // latency.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    // One tile from stage S (0 or 1, a compile-time constant): the next
+    // One tile from stage S = k & 1 (a compile-time constant): the next
     // tile's loads go to the other stage, which was last read before the
     // previous barrier. Direct loads complete before the barrier that ends
     // the step (the barrier waits for the wave's outstanding loads).
@@ -605,28 +635,14 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       uint16_t* vs_next = S ? Vs0 : Vs1;
       const bool more = k + 1 < ntiles;
       if (more) {
-        if constexpr (kDma) dma_tile(tile_pos(k + 1), ks_next, vs_next);
-        else load_tile(tile_pos(k + 1));
-      }
-      if (kTwoPhase && k == nlam) {
-        // end of the Lambda phase: keep (1 - alpha) * O / l (forward) or
-        // dout . O / l (gate gradient), restart the state
-        const float ll = l_f + __shfl_xor(l_f, 32, 64);
-        if constexpr (kGrad) {
-          g_lam = dout_dot(1.0f / ll);
+        if constexpr (kDma) {
+          dma_rows(tile_pos(k + 1), ks_next, krs, k_c16);
+          dma_rows(tile_pos(k + 1), vs_next, vrs, v_c16);
         } else {
-          const float wl = (1.0f - alpha) / ll;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              lam_at(db, i) = pack_bf16x2(o_f[db][2 * i] * wl, o_f[db][2 * i + 1] * wl);
+          load_tile(tile_pos(k + 1));
         }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
-        m_f = -INFINITY;
-        l_f = 0.0f;
       }
+      if (kTwoPhase && k == nlam) end_lambda_phase();
       f32x16 st[2];
       qk(ks, st);
       consume(k, st, vs);
