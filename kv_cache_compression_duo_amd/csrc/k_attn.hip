@@ -285,6 +285,10 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   constexpr int SPR = RB / 16;    // 16-byte slots per row
   constexpr int RPI = 64 / SPR;   // rows per 1 KB load
   constexpr int NIW = D / 64;     // loads per wave per tensor and tile
+  // the swizzles, the XOR addressing of the operand reads and the 8 x NIW
+  // loads covering a 64-row tile hold for these row sizes only
+  static_assert(D == 64 || D == 128, "direct-load layout: 128- or 256-byte rows");
+  static_assert(8 * NIW * RPI == kBN, "the block's loads cover one tile");
   auto ksw = [](int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
   auto vsw = [](int r) { return RB == 256 ? 2 * (r & 3) : (r & 3); };
   const int last_row = (MODE == MODE_RETRIEVAL ? a.n + a.T : a.T) - 1;
