@@ -154,8 +154,9 @@ __device__ __forceinline__ const uint16_t* stream_row(const AttnArgs& a, int b, 
   return (ring ? ring_base : in_base) + (chunk ? i_chunk : ring ? i_ring : i_mask) * D;
 }
 
-// Waves per block: 8 (each staged K/V tile serves 256 query rows; waves 0-3
-// stage V, waves 4-7 stage K).
+// Waves per block: 8 (each staged K/V tile serves 256 query rows; with
+// register staging waves 0-3 stage V and waves 4-7 K, with direct loads every
+// wave issues a share of both).
 template <int MODE>
 constexpr int attn_waves() { return 8; }
 
