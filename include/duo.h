@@ -182,9 +182,13 @@ duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t
  * [0, n+chunk_len); streaming heads attend under the Lambda mask over the ring
  * as it was before the chunk plus the chunk, then the ring is updated.
  * Writes out [B, chunk_len, Hq, D] bf16 and advances the token count.
- * Layers whose kv_dtype or retrieval_dtype is not BF16 return
- * DUO_ERR_UNSUPPORTED (fill such caches with duo_append_kv); so does a layer
- * whose sequences hold different counts (use duo_prefill_chunk_seq). */
+ * Every cache form is accepted: with an FP16 cache or ring the products take
+ * q converted to fp16 (exact for magnitudes in fp16's normal range) and fp16
+ * softmax weights; an INT4_G32 cache is attended in its decoded values
+ * fma(code, scale, zero), rounded to fp16 (the chunk is quantised into the
+ * cache first, so the chunk's own keys are decoded ones too).
+ * DUO_ERR_CAPACITY if n + chunk_len > capacity; DUO_ERR_UNSUPPORTED while the
+ * sequences hold different counts (use duo_prefill_chunk_seq). */
 duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,
                              int32_t chunk_len, void* out, hipStream_t stream);
 

@@ -310,7 +310,6 @@ duo_status duo_prefill_chunk(duo_layer* L, const void* q, const void* k, const v
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
     return st;
-  if (L->d.kv_dtype != DUO_BF16 || L->d.retrieval_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   if (L->ragged) return DUO_ERR_UNSUPPORTED;  // per sequence: duo_prefill_chunk_seq
   if (L->Hr > 0 && L->n + T > L->d.retrieval_capacity) return DUO_ERR_CAPACITY;
   if (L->n + T > (int64_t)INT32_MAX) return DUO_ERR_CAPACITY;
@@ -454,7 +453,6 @@ duo_status duo_prefill_chunk_seq(duo_layer* L, int32_t b, const void* q, const v
   if ((st = check_act(q)) != DUO_OK || (st = check_act(k)) != DUO_OK ||
       (st = check_act(v)) != DUO_OK || (st = check_act(out)) != DUO_OK)
     return st;
-  if (L->d.kv_dtype != DUO_BF16 || L->d.retrieval_dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   duo_layer view = sequence_view(L, b);
   if ((st = prefill_launch(&view, q, k, v, T, out, stream)) != DUO_OK) return st;
   advance_sequence(L, b, T);

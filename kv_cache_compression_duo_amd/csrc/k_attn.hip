@@ -50,6 +50,8 @@ namespace duo {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Kernel modes; the _BLOCK variants take the streaming part of the
@@ -60,8 +62,22 @@ enum {
   MODE_MIXED = 2,
   MODE_GRAD = 3,
   MODE_MIXED_BLOCK = 4,
-  MODE_GRAD_BLOCK = 5
+  MODE_GRAD_BLOCK = 5,
+  // fp16 forms of the prefill (layers with an fp16 or 4-bit cache): K/V tiles,
+  // P and the products in fp16; the 4-bit form dequantises its tiles on the
+  // way to LDS
+  MODE_RETRIEVAL_I4 = 6,
+  MODE_RETRIEVAL_F16 = 7,
+  MODE_STREAMING_F16 = 8
 };
+constexpr bool mode_f16(int m) {
+  return m == MODE_RETRIEVAL_I4 || m == MODE_RETRIEVAL_F16 || m == MODE_STREAMING_F16;
+}
+constexpr bool mode_streaming(int m) { return m == MODE_STREAMING || m == MODE_STREAMING_F16; }
+// causal attention of a chunk over the retrieval cache
+constexpr bool mode_cache(int m) {
+  return m == MODE_RETRIEVAL || m == MODE_RETRIEVAL_F16 || m == MODE_RETRIEVAL_I4;
+}
 
 struct AttnArgs {
   const uint16_t* q;     // [B][T][Hq][D]
@@ -72,6 +88,11 @@ struct AttnArgs {
   const uint16_t* vc;
   const uint16_t* kr;    // ring [B][Hs][S+R][D]
   const uint16_t* vr;
+  const uint8_t* kcodes;   // 4-bit retrieval cache (MODE_RETRIEVAL_I4): [B][Hr][cap32][D/2]
+  const uint8_t* vcodes;   // [B][Hr][cap32/32][16 D] in the decode's PV operand order
+  const uint32_t* ksz;     // [B][Hr][cap32/32][D/32][32] fp16 scale | fp16 zero << 16
+  const uint32_t* vsz;
+  int64_t cap32;
   const float* alpha;    // [Hkv] (mixed)
   const uint16_t* dout;  // [B][T][Hq][D] bf16 (gate gradient)
   float* partial;        // [B][head groups][query tiles] (gate gradient)
@@ -88,6 +109,29 @@ constexpr int kBN = 64;  // keys per tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Element-generic pieces: the kernels take K/V tiles (and P) as bf16, or as
+// fp16 for layers with an fp16 or 4-bit cache (Q, given as bf16, is converted;
+// every bf16 value with a normal fp16 exponent converts exactly).
+template <bool F16>
+using elem8 = std::conditional_t<F16, f16x8, bf16x8>;
+template <bool F16>
+__device__ __forceinline__ elem8<F16> as_elem8(const u32x4& v) {
+  return __builtin_bit_cast(elem8<F16>, v);
+}
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// c + a.x + a.y for a pair of softmax weights (v_dot2c against ones)
+__device__ __forceinline__ float add_pair(bf16x2 a, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, c, false);
+}
+__device__ __forceinline__ float add_pair(f16x2 a, float c) {
+  return __builtin_amdgcn_fdot2(a, f16x2{(_Float16)1.0f, (_Float16)1.0f}, c, false);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -172,13 +216,20 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   constexpr bool kMixed = MODE == MODE_MIXED || MODE == MODE_MIXED_BLOCK;
   constexpr bool kGrad = MODE == MODE_GRAD || MODE == MODE_GRAD_BLOCK;
   constexpr bool kBlock = MODE == MODE_MIXED_BLOCK || MODE == MODE_GRAD_BLOCK;
+  constexpr bool kStream = mode_streaming(MODE);
+  constexpr bool kCache = mode_cache(MODE);
+  constexpr bool kI4 = MODE == MODE_RETRIEVAL_I4;
+  constexpr bool kF16 = mode_f16(MODE);
+  using E8 = elem8<kF16>;  // MFMA operand: 8 bf16 or 8 fp16 values
+  using Elem = std::conditional_t<kF16, _Float16, __bf16>;
+  using E2 = std::conditional_t<kF16, f16x2, bf16x2>;
   // the gate-blended forward and its gate gradient visit the Lambda tiles,
   // then all causal tiles
   constexpr bool kTwoPhase = kMixed || kGrad;
   // Modes that read K and V through one buffer resource each stage them
   // with direct global->LDS loads (see below); streaming mode gathers rows
-  // per lane through registers.
-  constexpr bool kDma = MODE != MODE_STREAMING;
+  // per lane, and the 4-bit mode dequantises codes, through registers.
+  constexpr bool kDma = !kStream && !kI4;
   constexpr int KROW = kDma ? D : KPAD;  // K tile row stride in LDS (elements)
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
   // written to the other, so one barrier per tile suffices. The stages are
@@ -226,7 +277,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // query's block
   constexpr bool lblk = kBlock;
   const int sbk = (a.S + kBN - 1) / kBN, rbk = (a.R + kBN - 1) / kBN;
-  if constexpr (MODE != MODE_RETRIEVAL) {
+  if constexpr (!kCache) {
     const int lo0 = lblk ? (i_min / kBN - rbk + 1) * kBN : i_min - a.R + 1;
     const int lo = lo0 > 0 ? lo0 : 0;
     const int s_eff = lblk ? sbk * kBN : a.S;
@@ -236,17 +287,30 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     const int n2 = i_max >= w0 ? (i_max - w0) / kBN + 1 : 0;
     nlam = n1 + n2;
   }
-  ntiles = MODE == MODE_STREAMING ? nlam : nlam + i_max / kBN + 1;
+  ntiles = kStream ? nlam : nlam + i_max / kBN + 1;
   auto tile_pos = [&](int k) {
     return k < nlam ? (k < n1 ? kBN * k : w0 + kBN * (k - n1)) : kBN * (k - nlam);
   };
 
   // ---- query fragments (B operand of S^T = K Q^T) ----------------------------
-  bf16x8 qf[KS];
+  E8 qf[KS];
   {
     const uint16_t* qp = a.q + (((int64_t)b * a.T + t_qc) * a.Hq + head) * D + 8 * h2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qp + 16 * ks));
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w = ld16(qp + 16 * ks);
+      if constexpr (kF16) {
+        // bf16 -> fp32 (exact) -> fp16 (exact for magnitudes in fp16's normal
+        // range: a bf16 significand has 8 bits, fp16's 11)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t wi = word_of(w, i >> 1);
+          qf[ks][i] = (_Float16)__uint_as_float((i & 1) ? (wi & 0xffff0000u) : (wi << 16));
+        }
+      } else {
+        qf[ks] = as_bf16x8(w);
+      }
+    }
   }
 
   // ---- staging of one K/V tile ---------------------------------------------------
@@ -255,16 +319,15 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // (the host keeps every such range below 2^31 bytes). Retrieval mode reads
   // the head's cached rows, the mixed forward the sequence's rows of one KV
   // head (a row stride of Hkv*D).
-  const uint32_t rstride = (uint32_t)(MODE == MODE_RETRIEVAL ? D * 2 : a.Hkv * D * 2);
-  const int64_t hoff = MODE == MODE_RETRIEVAL ? ((int64_t)b * a.Hr + kv) * a.cap * D
-                                              : ((int64_t)b * a.T * a.Hkv + kv) * D;
-  const uint32_t rbytes =
-      MODE == MODE_RETRIEVAL ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2)
-                             : (uint32_t)((int64_t)a.T * a.Hkv - kv) * (uint32_t)(D * 2);
+  const uint32_t rstride = (uint32_t)(kCache ? D * 2 : a.Hkv * D * 2);
+  const int64_t hoff = kCache ? ((int64_t)b * a.Hr + kv) * a.cap * D
+                              : ((int64_t)b * a.T * a.Hkv + kv) * D;
+  const uint32_t rbytes = kCache ? (uint32_t)(a.n + a.T) * (uint32_t)(D * 2)
+                                 : (uint32_t)((int64_t)a.T * a.Hkv - kv) * (uint32_t)(D * 2);
   const __amdgpu_buffer_rsrc_t krs =
-      wave_rsrc((MODE == MODE_RETRIEVAL ? a.kc : a.k_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
+      wave_rsrc((kCache ? a.kc : a.k_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
   const __amdgpu_buffer_rsrc_t vrs =
-      wave_rsrc((MODE == MODE_RETRIEVAL ? a.vc : a.v_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
+      wave_rsrc((kCache ? a.vc : a.v_in) + (kDma ? hoff : 0), kDma ? rbytes : 0u);
 
   // Direct loads (kDma). A 16-byte buffer load with the LDS bit writes lane
   // i's data to the instruction's LDS base + 16 i, so a 1 KB block of a tile
@@ -292,7 +355,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   static_assert(8 * NIW * RPI == kBN, "the block's loads cover one tile");
   auto ksw = [](int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
   auto vsw = [](int r) { return RB == 256 ? 2 * (r & 3) : (r & 3); };
-  const int last_row = (MODE == MODE_RETRIEVAL ? a.n + a.T : a.T) - 1;
+  const int last_row = (kCache ? a.n + a.T : a.T) - 1;
   const int dma_row0 = wave * NIW * RPI + lane / SPR;  // this lane's row in the wave's first block
   uint32_t k_c16[NIW], v_c16[NIW];  // byte offset of the chunk a lane fetches within its row
 #pragma unroll
@@ -351,13 +414,117 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       dst[1] = hi;
     }
   };
-  auto load_tile = [&](int p0) {
-    if (stage_k) load_k(p0);
-    if (v_active) load_v(p0);
+
+  // 4-bit staging (retrieval heads of a 4-bit cache). The codes and the
+  // scale/zero words are loaded before the current tile's products and
+  // decoded as fma(code, scale, zero) in fp32, rounded to fp16, after them.
+  //   K: thread (row, quarter) takes the D/4 channels kr_d0 .. of key row
+  //      kr_row (D/8 code bytes, one group's scale/zero word), written to the
+  //      padded row layout above.
+  //   V: in a 32-token block the 16-byte code unit u = 4 (16 ch + cl) + mh
+  //      holds channels 64 ch + 16 cq + cl (cq = 0..3, byte 4 cq + i) of
+  //      tokens 4 mh + i (low nibbles) and 16 + 4 mh + i (high nibbles); a
+  //      tile is two blocks, D units each, one unit per thread. Its 4 x 8
+  //      values become eight 4-key chunks of V^T rows (vt_slot).
+  // Rows past the last key: K rows are clamped to it (finite, masked); V
+  // values are set to zero (the scale/zero words of unwritten rows are not
+  // data), blocks past the last one clamped to it so every read stays inside
+  // the head's arrays.
+  const int64_t bh = (int64_t)b * a.Hr + kv;
+  const int nblk32 = (int)(a.cap32 >> 5);
+  const int vi_b2 = st_t / D, vi_u = st_t % D;  // V: block of the tile, code unit
+  const int vi_mh = vi_u & 3, vi_cl = (vi_u >> 2) & 15, vi_ch = vi_u >> 6;
+  const bool vi_active = !stage_k && st_t < 2 * D;
+  constexpr int KCW = D / 32;  // code words (8 channels each) of a K thread
+  uint32_t kcode[KCW], kszw = 0;
+  u32x4 vcode = {}, vszq[4] = {};
+  auto load_k_i4 = [&](int p0) {
+    int r = p0 + kr_row;
+    r = r < last_row ? r : last_row;
+    const uint32_t* cp =
+        reinterpret_cast<const uint32_t*>(a.kcodes + (bh * a.cap32 + r) * (D / 2) + kr_d0 / 2);
+#pragma unroll
+    for (int i = 0; i < KCW; ++i) kcode[i] = cp[i];
+    kszw = a.ksz[((bh * nblk32 + (r >> 5)) * (D / 32) + kr_d0 / 32) * 32 + (r & 31)];
   };
-  auto store_tile = [&](uint16_t* ks, uint16_t* vt) {
-    if (stage_k) store_k(ks);
-    if (v_active) store_v(vt);
+  auto store_k_i4 = [&](uint16_t* ks) __attribute__((always_inline)) {
+    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(kszw & 0xffffu));
+    const float zp = (float)__builtin_bit_cast(_Float16, (uint16_t)(kszw >> 16));
+#pragma unroll
+    for (int i = 0; i < KCW; ++i) {
+      // byte j of word i: channels 8 i + 2 j (low nibble) and 8 i + 2 j + 1
+      const uint32_t lo = kcode[i] & 0x0f0f0f0fu, hi = (kcode[i] >> 4) & 0x0f0f0f0fu;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 h = {(_Float16)fmaf((float)((lo >> (8 * j)) & 0xffu), sc, zp),
+                         (_Float16)fmaf((float)((hi >> (8 * j)) & 0xffu), sc, zp)};
+        w[j] = __builtin_bit_cast(uint32_t, h);
+      }
+      st16(ks + kr_row * KPAD + kr_d0 + 8 * i, u32x4{w[0], w[1], w[2], w[3]});
+    }
+  };
+  auto load_v_i4 = [&](int p0) {
+    int blk = (p0 >> 5) + vi_b2;
+    blk = blk < (last_row >> 5) ? blk : (last_row >> 5);
+    const int64_t bb = bh * nblk32 + blk;
+    vcode = ld16(a.vcodes + bb * (16 * D) + 16 * vi_u);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+        vszq[2 * gi + run] =
+            ld16(a.vsz + (bb * (D / 32) + 2 * vi_ch + gi) * 32 + 16 * run + 4 * vi_mh);
+  };
+  auto store_v_i4 = [&](uint16_t* vt, int p0) __attribute__((always_inline)) {
+    const int tok0 = p0 + 32 * vi_b2 + 4 * vi_mh;  // token of run 0, i = 0
+#pragma unroll
+    for (int cq = 0; cq < 4; ++cq) {
+      const int d = 64 * vi_ch + 16 * cq + vi_cl;
+      const uint32_t cw = word_of(vcode, cq);
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        const uint32_t nib = run ? (cw >> 4) & 0x0f0f0f0fu : cw & 0x0f0f0f0fu;
+        const u32x4& sz = vszq[2 * (cq >> 1) + run];
+        _Float16 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = tok0 + 16 * run + i <= last_row;
+          const uint32_t w = ok ? word_of(sz, i) : 0u;  // scale = zero = 0: value 0
+          x[i] = (_Float16)fmaf((float)((nib >> (8 * i)) & 0xffu),
+                                (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)),
+                                (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)));
+        }
+        const int c4 = 8 * vi_b2 + 4 * run + vi_mh;  // 4-key chunk of the tile
+        uint2 o;
+        o.x = __builtin_bit_cast(uint32_t, f16x2{x[0], x[1]});
+        o.y = __builtin_bit_cast(uint32_t, f16x2{x[2], x[3]});
+        *reinterpret_cast<uint2*>(vt + d * kBN + 4 * vt_slot(c4, d)) = o;
+      }
+    }
+  };
+
+  int staged_p0 = 0;  // position of the tile held in the staging registers
+  auto load_tile = [&](int p0) {
+    if constexpr (kI4) {
+      staged_p0 = p0;
+      if (stage_k) load_k_i4(p0);
+      if (vi_active) load_v_i4(p0);
+    } else {
+      if (stage_k) load_k(p0);
+      if (v_active) load_v(p0);
+    }
+  };
+  // (always_inline: the compiler outlined the 4-bit form, moving every
+  // captured staging register to scratch memory)
+  auto store_tile = [&](uint16_t* ks, uint16_t* vt) __attribute__((always_inline)) {
+    if constexpr (kI4) {
+      if (stage_k) store_k_i4(ks);
+      if (vi_active) store_v_i4(vt, staged_p0);
+    } else {
+      if (stage_k) store_k(ks);
+      if (v_active) store_v(vt);
+    }
   };
 
   // ---- state --------------------------------------------------------------------
@@ -424,7 +591,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       m = mn;
     }
   };
-  auto softmax_weights = [&](const f32x16 (&sc)[2], float m, float& l, bf16x8 (&pb)[4]) {
+  auto softmax_weights = [&](const f32x16 (&sc)[2], float m, float& l, E8 (&pb)[4]) {
     const float mc = m == -INFINITY ? 0.0f : m * c2;  // no allowed key yet: p = 0
     float p[2][16];
 #pragma unroll
@@ -434,22 +601,20 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)p[s >> 1][8 * (s & 1) + i];
-    // the row sum adds the bf16 values the PV product uses, two per dot2
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      for (int i = 0; i < 8; ++i) pb[s][i] = (Elem)p[s >> 1][8 * (s & 1) + i];
+    // the row sum adds the rounded values the PV product uses, two per dot2
     float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int i = 0; i < 8; i += 4) {
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[s][i], pb[s][i + 1]}, ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[s][i + 2], pb[s][i + 3]}, ones, ls1,
-                                              false);
+        ls0 = add_pair(E2{pb[s][i], pb[s][i + 1]}, ls0);
+        ls1 = add_pair(E2{pb[s][i + 2], pb[s][i + 3]}, ls1);
       }
     l += ls0 + ls1;
   };
   auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB],
-                            bf16x8 (&pb)[4]) {
+                            E8 (&pb)[4]) {
     softmax_rescale(sc, m, l, O);
     softmax_weights(sc, m, l, pb);
   };
@@ -463,13 +628,13 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const int c16 = lane & 15, dsub = (lane >> 4) & 1;
   const uint32_t v_lane = (uint32_t)((4 * h2 + (c16 >> 2)) * RB + ((dsub ^ vsw(c16 >> 2)) << 5) +
                                      ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8);
-  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[4], f32x16 (&O)[DB]) {
+  auto pv = [&](const uint16_t* vt, const E8 (&pb)[4], f32x16 (&O)[DB]) {
     // all V^T fragments of two 16-key slices are requested before their
     // products (the empty asm keeps the compiler from sinking each read next
     // to its use, which would expose the LDS latency between products)
 #pragma unroll
     for (int s2 = 0; s2 < 4; s2 += 2) {
-      bf16x8 av[2][DB];
+      E8 av[2][DB];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -477,11 +642,11 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
           if constexpr (kDma) {
             const char* p = reinterpret_cast<const char*>(vt) + (v_lane ^ (uint32_t)(db << 6)) +
                             16 * (s2 + h) * RB;
-            av[h][db] = lds_tr_pair(p, p + 8 * RB);
+            av[h][db] = __builtin_bit_cast(E8, lds_tr_pair(p, p + 8 * RB));
           } else {
             // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
             const int d = 32 * db + q32;
-            av[h][db] = as_bf16x8(
+            av[h][db] = as_elem8<kF16>(
                 *reinterpret_cast<const u32x4*>(vt + d * kBN + 4 * vt_slot(4 * (s2 + h) + h2, d)));
           }
         }
@@ -490,7 +655,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[h][db], pb[s2 + h], O[db], 0, 0, 0);
+          O[db] = mma32(av[h][db], pb[s2 + h], O[db]);
     }
   };
 
@@ -505,16 +670,16 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   auto qk = [&](const uint16_t* ks, f32x16 (&st)[2]) {
     st[0] = f32x16{};
     st[1] = f32x16{};
-    bf16x8 ak0[KS], ak1[KS];
+    E8 ak0[KS], ak1[KS];
     if constexpr (kDma) {
       const char* kb = reinterpret_cast<const char*>(ks);
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5))));
+        ak0[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5))));
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak1[ks_] = as_bf16x8(
+        ak1[ks_] = as_elem8<kF16>(
             *reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5)) + 32 * RB));
       asm volatile("" ::: "memory");
     } else {
@@ -522,17 +687,17 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       const uint16_t* krow1 = krow0 + 32 * KPAD;
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak0[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks_));
+        ak0[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(krow0 + 16 * ks_));
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak1[ks_] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks_));
+        ak1[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(krow1 + 16 * ks_));
       asm volatile("" ::: "memory");
     }
 #pragma unroll
     for (int ks_ = 0; ks_ < KS; ++ks_) {
-      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0[ks_], qf[ks_], st[0], 0, 0, 0);
-      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1[ks_], qf[ks_], st[1], 0, 0, 0);
+      st[0] = mma32(ak0[ks_], qf[ks_], st[0]);
+      st[1] = mma32(ak1[ks_], qf[ks_], st[1]);
     }
   };
   // Causal / Lambda mask of tile k's raw scores, in place (unmasked tiles
@@ -541,7 +706,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // first query need none.
   auto mask_scores = [&](int k, f32x16 (&st)[2]) {
     const int p0 = tile_pos(k);
-    const bool lam_phase = MODE == MODE_STREAMING || (kTwoPhase && k < nlam);
+    const bool lam_phase = kStream || (kTwoPhase && k < nlam);
     const bool diag = p0 + kBN - 1 > i_wfirst;
     if (lam_phase || diag) {
       // Element j of the lane's scores is key base + c_j, with c_j a
@@ -550,7 +715,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       // every tile). Bitwise operators: a select per element, no per-lane
       // branches.
       const int base = p0 + 4 * h2;
-      if constexpr (MODE == MODE_RETRIEVAL || lblk) {
+      if constexpr (kCache || lblk) {
         // causal: c_j <= dq; under the block mask a 64-key tile is one
         // block, visible to a query or not as a whole
         int dq = i_q - base;
@@ -586,7 +751,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   auto consume = [&](int k, f32x16 (&st)[2], const uint16_t* vt) {
     if (tile_pos(k) <= i_wlast) {
       mask_scores(k, st);
-      bf16x8 pb[4];
+      E8 pb[4];
       softmax_update(st, m_f, l_f, o_f, pb);
       pv(vt, pb, o_f);
     }
@@ -720,7 +885,7 @@ static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
   // different heads lose the L2 reuse of one head's ring and chunk rows: query
   // tiles in x ran 42 instead of 59 us per 8192-token chunk of the Llama-3-8B
   // layer. The y extent of a grid is 16 bits.
-  x.tiles_in_y = MODE != MODE_STREAMING && x.n_qtiles <= 65535;
+  x.tiles_in_y = !mode_streaming(MODE) && x.n_qtiles <= 65535;
   dim3 grid(x.tiles_in_y ? hgs : (unsigned)x.n_qtiles, x.tiles_in_y ? (unsigned)x.n_qtiles : hgs,
             (unsigned)B);
   attn_kernel<D, HB, MODE><<<grid, 64 * NW, 0, s>>>(x);
@@ -769,7 +934,18 @@ hipError_t launch_prefill_retrieval(const duo_layer* L, const void* q, int T, vo
                                     hipStream_t s) {
   AttnArgs a = base_args(L, q, T, out);
   a.kv_base = 0;
-  return launch_mode<MODE_RETRIEVAL>(a, L->d.head_dim, L->Hr, L->d.batch, s);
+  const int D = L->d.head_dim;
+  if (L->d.retrieval_dtype == DUO_INT4_G32) {
+    a.kcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.k_offset);
+    a.vcodes = reinterpret_cast<const uint8_t*>(L->rbuf + L->lay.v_offset);
+    a.ksz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.k_sz_offset);
+    a.vsz = reinterpret_cast<const uint32_t*>(L->rbuf + L->lay.v_sz_offset);
+    a.cap32 = cap32_of(L->d.retrieval_capacity);
+    return launch_mode<MODE_RETRIEVAL_I4>(a, D, L->Hr, L->d.batch, s);
+  }
+  return L->d.retrieval_dtype == DUO_FP16
+             ? launch_mode<MODE_RETRIEVAL_F16>(a, D, L->Hr, L->d.batch, s)
+             : launch_mode<MODE_RETRIEVAL>(a, D, L->Hr, L->d.batch, s);
 }
 
 hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const void* k,
@@ -778,7 +954,9 @@ hipError_t launch_prefill_streaming(const duo_layer* L, const void* q, const voi
   a.k_in = static_cast<const uint16_t*>(k);
   a.v_in = static_cast<const uint16_t*>(v);
   a.kv_base = L->Hr;
-  return launch_mode<MODE_STREAMING>(a, L->d.head_dim, L->Hs, L->d.batch, s);
+  return L->d.kv_dtype == DUO_FP16
+             ? launch_mode<MODE_STREAMING_F16>(a, L->d.head_dim, L->Hs, L->d.batch, s)
+             : launch_mode<MODE_STREAMING>(a, L->d.head_dim, L->Hs, L->d.batch, s);
 }
 
 hipError_t launch_mixed(const duo_layer_desc& d, const void* q, const void* k, const void* v,

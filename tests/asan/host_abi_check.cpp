@@ -106,12 +106,23 @@ static void token_counts_and_failures() {
   CHECK(duo_layer_destroy(L) == DUO_OK);
   CHECK(duo_layer_destroy(nullptr) == DUO_OK);
   CHECK(duo_layer_tokens(nullptr) == -1);
-  // prefill of a 16-bit fp16 or 4-bit layer is not implemented
-  duo_layer_desc d16 = desc(1, 8, 8, 64, 2, 100, DUO_FP16, DUO_FP16);
-  CHECK(duo_layer_init(&L, &d16, dev(1), dev(2), dev(3), 0, nullptr) == DUO_OK);
-  CHECK(duo_prefill_chunk(L, dev(6), dev(4), dev(5), 3, dev(7), nullptr) == DUO_ERR_UNSUPPORTED);
-  CHECK(duo_layer_tokens(L) == 0);
-  duo_layer_destroy(L);
+  // fp16 and 4-bit layers prefill like bf16 ones: the cache append, both
+  // attention launches and the ring append, then the count advances
+  const duo_dtype forms[3][2] = {{DUO_FP16, DUO_FP16}, {DUO_FP16, DUO_INT4_G32},
+                                 {DUO_BF16, DUO_INT4_G32}};
+  for (const auto& f : forms) {
+    duo_layer_desc dq = desc(1, 8, 8, 64, 2, 100, f[0], f[1]);
+    CHECK(duo_layer_init(&L, &dq, dev(1), dev(2), dev(3), 0, nullptr) == DUO_OK);
+    g_stub.reset();
+    CHECK(duo_prefill_chunk(L, dev(6), dev(4), dev(5), 3, dev(7), nullptr) == DUO_OK);
+    CHECK(g_stub.calls[duo::kAppendCache] == 1 && g_stub.calls[duo::kPrefillRetrieval] == 1 &&
+          g_stub.calls[duo::kPrefillStreaming] == 1 && g_stub.calls[duo::kAppendRing] == 1);
+    CHECK(duo_layer_tokens(L) == 3);
+    CHECK(duo_prefill_chunk(L, dev(6), dev(4), dev(5), 98, dev(7), nullptr) == DUO_ERR_CAPACITY);
+    CHECK(duo_layer_tokens(L) == 3);
+    duo_layer_destroy(L);
+  }
+  g_stub.reset();
   // init validation
   CHECK(duo_layer_init(&L, &d, dev(1), dev(2), nullptr, 0, nullptr) == DUO_ERR_INVALID_ARG);
   CHECK(duo_layer_init(&L, &d, (char*)dev(1) + 16, dev(2), dev(3), 0, nullptr) == DUO_ERR_LAYOUT);

@@ -163,16 +163,3 @@ def test_chunked_equals_one_shot_on_gpu():
     d = (outs[0] - outs[1]).abs().max().item()
     say(f"  chunked vs one-shot max diff {d:.3e}")
     assert d <= 2e-2
-
-
-def test_prefill_rejects_fp16_layer():
-    import kv_cache_compression_duo_amd as duo
-    dev = device()
-    lay = duo.DuoLayer(n_q_heads=4, n_kv_heads=2, head_dim=64, n_retrieval_kv_heads=1,
-                       capacity=16, softmax_scale=0.125, kv_dtype="fp16", device=dev)
-    q = torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16, device=dev)
-    kv = torch.zeros(1, 4, 2, 64, dtype=torch.float16, device=dev)
-    with pytest.raises(duo.DuoError) as e:
-        lay.prefill_chunk(q, kv, kv)
-    assert e.value.status == 2
-    assert lay.n_tokens == 0
