@@ -358,23 +358,37 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const int last_row = (kCache ? a.n + a.T : a.T) - 1;
   const int dma_row0 = wave * NIW * RPI + lane / SPR;  // this lane's row in the wave's first block
   uint32_t k_c16[NIW], v_c16[NIW];  // byte offset of the chunk a lane fetches within its row
+  uint32_t k_lo[NIW], v_lo[NIW];    // and of that chunk within the tile (row offset added)
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int r = dma_row0 + j * RPI, pos = lane % SPR;
     k_c16[j] = (uint32_t)(pos ^ ksw(r)) * 16u;
     v_c16[j] = (uint32_t)(2 * ((pos >> 1) ^ vsw(r)) + (pos & 1)) * 16u;
+    k_lo[j] = (uint32_t)r * rstride + k_c16[j];
+    v_lo[j] = (uint32_t)r * rstride + v_c16[j];
   }
-  // the rows p0 .. p0 + 63 of one tensor into the stage at dst
+  // the rows p0 .. p0 + 63 of one tensor into the stage at dst. A tile
+  // wholly before the last key takes its row offset as the scalar offset and
+  // the lane's offset within the tile from a register (no address VALU per
+  // tile); the last tile clamps each lane's row to the last key.
   auto dma_rows = [&](int p0, uint16_t* dst, __amdgpu_buffer_rsrc_t rs,
-                      const uint32_t (&c16)[NIW]) {
+                      const uint32_t (&c16)[NIW], const uint32_t (&lo)[NIW]) {
+    if (p0 + kBN - 1 <= last_row) {
+      const uint32_t so = (uint32_t)p0 * rstride;  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-      const int blk = wave * NIW + j;  // the wave's j-th 1 KB block of the tile
-      int r = p0 + dma_row0 + j * RPI;
-      r = r < last_row ? r : last_row;
-      const uint32_t ro = (uint32_t)r * rstride;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + blk * 512), 16, (int)(ro + c16[j]),
-                                               0, 0, 0);
+      for (int j = 0; j < NIW; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + (wave * NIW + j) * 512), 16,
+                                                 (int)lo[j], (int)so, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NIW; ++j) {
+        const int blk = wave * NIW + j;  // the wave's j-th 1 KB block of the tile
+        int r = p0 + dma_row0 + j * RPI;
+        r = r < last_row ? r : last_row;
+        const uint32_t ro = (uint32_t)r * rstride;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst + blk * 512), 16,
+                                                 (int)(ro + c16[j]), 0, 0, 0);
+      }
     }
   };
 
@@ -578,7 +592,13 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sc[kb][j]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    {
+      // lanes l and l + 32 hold the two halves of a query's keys: one
+      // v_permlane32_swap gives every lane its partner's maximum
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm),
+                                                       false, false);
+      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mn = fmaxf(m, tm);
     // m = -inf (no allowed key yet) and a finite tm always rescales
     if (__ballot(tm > m + lazy) != 0) {
@@ -779,8 +799,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // ---- main loop ----------------------------------------------------------------
   {
     if constexpr (kDma) {
-      dma_rows(tile_pos(0), Ks0, krs, k_c16);
-      dma_rows(tile_pos(0), Vs0, vrs, v_c16);
+      dma_rows(tile_pos(0), Ks0, krs, k_c16, k_lo);
+      dma_rows(tile_pos(0), Vs0, vrs, v_c16, v_lo);
     } else {
       load_tile(tile_pos(0));
       store_tile(Ks0, Vs0);
@@ -806,8 +826,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       const bool more = k + 1 < ntiles;
       if (more) {
         if constexpr (kDma) {
-          dma_rows(tile_pos(k + 1), ks_next, krs, k_c16);
-          dma_rows(tile_pos(k + 1), vs_next, vrs, v_c16);
+          dma_rows(tile_pos(k + 1), ks_next, krs, k_c16, k_lo);
+          dma_rows(tile_pos(k + 1), vs_next, vrs, v_c16, v_lo);
         } else {
           load_tile(tile_pos(k + 1));
         }
