@@ -553,6 +553,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
   for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
   float m_f = -INFINITY, l_f = 0.0f;
+  float mc_f = 0.0f;  // m_f * scale_log2, or 0 while m_f = -inf (no allowed key yet)
   __shared__ uint32_t lam_lds[kMixed ? NW * DB * 8 * 64 : 1];
   auto lam_at = [&](int db, int i) -> uint32_t& {
     return lam_lds[((wave * DB + db) * 8 + i) * 64 + lane];
@@ -586,7 +587,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // B operands of the four 16-key slices.
   const float c2 = a.scale_log2;
   const float lazy = 8.0f / c2;  // raw-score growth that forces a rescale
-  auto softmax_rescale = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB]) {
+  auto softmax_rescale = [&](const f32x16 (&sc)[2], float& m, float& mc, float& l,
+                             f32x16 (&O)[DB]) {
     float tm = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -597,7 +599,11 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       // v_permlane32_swap gives every lane its partner's maximum
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm),
                                                        false, false);
-      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // one v_max_f32 of the pair (scores are never NaN, so the two
+      // quieting maxima the compiler puts around values it did not produce
+      // itself are not needed)
+      asm("v_max_f32 %0, %1, %2" : "=v"(tm) : "v"(__uint_as_float(sw[0])),
+          "v"(__uint_as_float(sw[1])));
     }
     const float mn = fmaxf(m, tm);
     // m = -inf (no allowed key yet) and a finite tm always rescales
@@ -609,10 +615,10 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
       for (int db = 0; db < DB; ++db) O[db] *= corr;
       m = mn;
+      mc = mn == -INFINITY ? 0.0f : mn * c2;
     }
   };
-  auto softmax_weights = [&](const f32x16 (&sc)[2], float m, float& l, E8 (&pb)[4]) {
-    const float mc = m == -INFINITY ? 0.0f : m * c2;  // no allowed key yet: p = 0
+  auto softmax_weights = [&](const f32x16 (&sc)[2], float mc, float& l, E8 (&pb)[4]) {
     float p[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -623,7 +629,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[s][i] = (Elem)p[s >> 1][8 * (s & 1) + i];
     // the row sum adds the rounded values the PV product uses, two per dot2
-    float ls0 = 0.0f, ls1 = 0.0f;
+    // (two chains, the first continuing from l)
+    float ls0 = l, ls1 = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -631,12 +638,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
         ls0 = add_pair(E2{pb[s][i], pb[s][i + 1]}, ls0);
         ls1 = add_pair(E2{pb[s][i + 2], pb[s][i + 3]}, ls1);
       }
-    l += ls0 + ls1;
+    l = ls0 + ls1;
   };
-  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& l, f32x16 (&O)[DB],
-                            E8 (&pb)[4]) {
-    softmax_rescale(sc, m, l, O);
-    softmax_weights(sc, m, l, pb);
+  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& mc, float& l,
+                            f32x16 (&O)[DB], E8 (&pb)[4]) {
+    softmax_rescale(sc, m, mc, l, O);
+    softmax_weights(sc, mc, l, pb);
   };
   // V^T fragment of lane (q32, h2) for slice s and d-block db: channel
   // 32 db + q32 of keys 16s + 4 h2 .. + 3 and 16s + 8 + 4 h2 .. + 3. In the
@@ -772,7 +779,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     if (tile_pos(k) <= i_wlast) {
       mask_scores(k, st);
       E8 pb[4];
-      softmax_update(st, m_f, l_f, o_f, pb);
+      softmax_update(st, m_f, mc_f, l_f, o_f, pb);
       pv(vt, pb, o_f);
     }
   };
@@ -793,6 +800,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
     for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
     m_f = -INFINITY;
+    mc_f = 0.0f;
     l_f = 0.0f;
   };
 
