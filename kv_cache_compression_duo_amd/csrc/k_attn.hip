@@ -198,6 +198,17 @@ __device__ __forceinline__ const uint16_t* stream_row(const AttnArgs& a, int b, 
   return (ring ? ring_base : in_base) + (chunk ? i_chunk : ring ? i_ring : i_mask) * D;
 }
 
+// Row lookup of streaming mode for a tile that starts inside the chunk: the
+// chunk's row, positions past its end clamped to its last row (masked: a key
+// after every query of the launch).
+template <int D>
+__device__ __forceinline__ const uint16_t* chunk_row(const AttnArgs& a, int b, int kv, int p,
+                                                     bool v) {
+  const int last = a.n + a.T - 1;
+  const int t = (p < last ? p : last) - a.n;
+  return wave_ptr(v ? a.v_in : a.k_in) + (((int64_t)b * a.T + t) * a.Hkv + kv) * D;
+}
+
 // Waves per block: 8 (each staged K/V tile serves 256 query rows; with
 // register staging waves 0-3 stage V and waves 4-7 K, with direct loads every
 // wave issues a share of both).
@@ -402,15 +413,27 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const bool v_active = !stage_k && vdc < D / 8;
   u32x4 kreg[4];  // K: KLD chunks of a row (unused, and removed, in the direct modes)
   u32x4 vown[4];  // V: one d-chunk of 4 keys
+  // (tiles that start inside the chunk, p0 >= n, a wave-uniform test, read
+  // chunk rows only)
   auto load_k = [&](int p0) {
-    const uint16_t* kp = stream_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
+    const uint16_t* kp;
+    if (p0 >= a.n)
+      kp = chunk_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
+    else
+      kp = stream_row<D>(a, b, kv, p0 + kr_row, false) + kr_d0;
 #pragma unroll
     for (int c = 0; c < KLD; ++c) kreg[c] = ld16(kp + 8 * c);
   };
   auto load_v = [&](int p0) {
+    if (p0 >= a.n) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      vown[r] = ld16(stream_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+      for (int r = 0; r < 4; ++r)
+        vown[r] = ld16(chunk_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vown[r] = ld16(stream_row<D>(a, b, kv, p0 + 4 * vg + r, true) + 8 * vdc);
+    }
   };
   auto store_k = [&](uint16_t* ks) {
 #pragma unroll
@@ -756,6 +779,17 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
           for (int j = 0; j < 16; ++j) {
             const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
             st[kb][j] = c <= dq ? st[kb][j] : -INFINITY;
+          }
+      } else if (lam_phase && p0 >= a.S) {
+        // token-level Lambda on a tile past the sinks: the window band
+        // 0 <= i - j < R, one unsigned compare of dq - c_j against R
+        const int dq = i_q - base;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = 32 * kb + 8 * (j >> 2) + (j & 3);
+            st[kb][j] = (uint32_t)(dq - c) < (uint32_t)a.R ? st[kb][j] : -INFINITY;
           }
       } else {
         // token-level Lambda; outside the Lambda phase every key passes the
