@@ -909,10 +909,17 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     }
     return;
   }
-  if (t_q >= a.T) return;
+  // The wave's 32 output rows (its tokens of one head) go through LDS, so the
+  // stores are whole rows, 64 / (D/8) rows per instruction, instead of 16
+  // bytes in each of 32 rows (Hq*D*2 bytes apart) per instruction. The tile
+  // stages are free after the loop's last barrier; each wave uses 32*D
+  // elements of one of them (16-byte chunks XOR-swizzled by row). Rows of
+  // tokens past the chunk are staged but not stored.
   const float lf = l_f + __shfl_xor(l_f, 32, 64);
   const float wf = alpha / lf;  // alpha = 1 outside the mixed forward
-  uint16_t* op = a.out + (((int64_t)b * a.T + t_q) * a.Hq + head) * D;
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static_assert(2 * 32 * D <= kBN * KROW && 2 * 32 * D <= D * kBN, "two waves per stage");
+  uint16_t* stg = (wave < 2 ? Ks0 : wave < 4 ? Ks1 : wave < 6 ? Vs0 : Vs1) + (wave & 1) * 32 * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -929,8 +936,19 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       uint2 w;
       w.x = pack_bf16x2(v[0], v[1]);
       w.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(op + 32 * db + 8 * jb + 4 * h2) = w;
+      const int ch = (4 * db + jb) ^ (q32 & (CPR - 1));  // channels 32 db + 8 jb ..
+      *reinterpret_cast<uint2*>(stg + q32 * D + 8 * ch + 4 * h2) = w;
     }
+  __syncthreads();
+  constexpr int RPS = 64 / CPR;  // rows per store instruction
+  const int lr = lane / CPR, lc = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPS; ++i) {
+    const int row = i * RPS + lr, tok = w_tok0 + row;
+    const u32x4 val =
+        *reinterpret_cast<const u32x4*>(stg + row * D + 8 * (lc ^ (row & (CPR - 1))));
+    if (tok < a.T) st16(a.out + (((int64_t)b * a.T + tok) * a.Hq + head) * D + 8 * lc, val);
+  }
 }
 
 // ---- launchers -------------------------------------------------------------------
