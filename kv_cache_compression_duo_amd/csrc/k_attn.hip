@@ -678,6 +678,17 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   const int c16 = lane & 15, dsub = (lane >> 4) & 1;
   const uint32_t v_lane = (uint32_t)((4 * h2 + (c16 >> 2)) * RB + ((dsub ^ vsw(c16 >> 2)) << 5) +
                                      ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8);
+  // The XOR'd lane offsets of the operand reads, computed once. In the
+  // gate-blended forward they are kept in registers behind an empty asm the
+  // compiler cannot look through: under that mode's register pressure it
+  // rebuilt each address with a v_or before every read (48 VALU per tile);
+  // the other modes keep them by themselves.
+  uint32_t v_off[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    v_off[db] = v_lane ^ (uint32_t)(db << 6);
+    if constexpr (kMixed) asm volatile("" : "+v"(v_off[db]));
+  }
   auto pv = [&](const uint16_t* vt, const E8 (&pb)[4], f32x16 (&O)[DB]) {
     // all V^T fragments of two 16-key slices are requested before their
     // products (the empty asm keeps the compiler from sinking each read next
@@ -690,8 +701,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           if constexpr (kDma) {
-            const char* p = reinterpret_cast<const char*>(vt) + (v_lane ^ (uint32_t)(db << 6)) +
-                            16 * (s2 + h) * RB;
+            const char* p = reinterpret_cast<const char*>(vt) + v_off[db] + 16 * (s2 + h) * RB;
             av[h][db] = __builtin_bit_cast(E8, lds_tr_pair(p, p + 8 * RB));
           } else {
             // keys 16s+4h2..+3 and 16s+8+4h2..+3: one adjacent 16-byte pair
@@ -717,6 +727,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // q32 and q32 + 32; in the direct layout at slot (2 ks_ + h2) ^ ksw(q32)
   // (ksw(q32 + 32) = ksw(q32)), an XOR of k_lane by 32 ks_.
   const uint32_t k_lane = (uint32_t)(q32 * RB + ((h2 ^ ksw(q32)) << 4));
+  uint32_t k_off[KS];
+#pragma unroll
+  for (int ks_ = 0; ks_ < KS; ++ks_) {
+    k_off[ks_] = k_lane ^ (uint32_t)(ks_ << 5);
+    if constexpr (kMixed) asm volatile("" : "+v"(k_off[ks_]));
+  }
   auto qk = [&](const uint16_t* ks, f32x16 (&st)[2]) {
     st[0] = f32x16{};
     st[1] = f32x16{};
@@ -725,12 +741,11 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       const char* kb = reinterpret_cast<const char*>(ks);
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak0[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5))));
+        ak0[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(kb + k_off[ks_]));
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int ks_ = 0; ks_ < KS; ++ks_)
-        ak1[ks_] = as_elem8<kF16>(
-            *reinterpret_cast<const u32x4*>(kb + (k_lane ^ (uint32_t)(ks_ << 5)) + 32 * RB));
+        ak1[ks_] = as_elem8<kF16>(*reinterpret_cast<const u32x4*>(kb + k_off[ks_] + 32 * RB));
       asm volatile("" ::: "memory");
     } else {
       const uint16_t* krow0 = ks + q32 * KPAD + 8 * h2;
