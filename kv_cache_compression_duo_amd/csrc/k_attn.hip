@@ -247,10 +247,14 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // separate arrays, each named statically in the (twice unrolled) loop, so
   // the compiler sees that reads of one stage do not wait for the direct
   // loads into the other.
-  __shared__ __align__(16) uint16_t Ks0[kBN * KROW];
-  __shared__ __align__(16) uint16_t Ks1[kBN * KROW];
-  __shared__ __align__(16) uint16_t Vs0[D * kBN];
-  __shared__ __align__(16) uint16_t Vs1[D * kBN];
+  // (32-byte alignment: LDS variables are laid out by alignment, then size,
+  // so the stages come before the gate-blended forward's 64 KB parking array
+  // and stay below 64 KB, where a read's 16-bit immediate offset reaches them;
+  // above it every operand address took a v_add)
+  __shared__ __align__(32) uint16_t Ks0[kBN * KROW];
+  __shared__ __align__(32) uint16_t Ks1[kBN * KROW];
+  __shared__ __align__(32) uint16_t Vs0[D * kBN];
+  __shared__ __align__(32) uint16_t Vs1[D * kBN];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
