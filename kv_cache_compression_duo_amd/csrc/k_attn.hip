@@ -1,5 +1,5 @@
-// Tiled softmax attention on bf16 MFMA for the prefill paths and the
-// gate-blended identification forward.
+// Tiled softmax attention on MFMA (bf16, or fp16 for fp16 and 4-bit caches)
+// for the prefill paths and the gate-blended identification forward.
 //
 // What is computed (xllm-io review "DuoAttention: Efficient Long-Context LLM
 // Inference with Retrieval and Streaming Heads", section 三 核心公式):
@@ -25,7 +25,8 @@
 //     query tile) first, folded into (1 - alpha) * O / l kept as bf16 pairs,
 //     then all causal tiles as in retrieval mode (the band's QK products are
 //     computed twice; two sets of accumulators would halve the occupancy);
-//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16. In this
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (the f16
+//     form for fp16 and 4-bit caches). In this
 //     orientation a lane holds one query's scores, so the softmax needs one
 //     cross-lane exchange per tile, and the score accumulator is directly the
 //     B operand of the PV product (keys permuted inside each 16-key slice,
@@ -36,10 +37,12 @@
 //     XOR-swizzled by row. K fragments are one ds_read_b128 each; V^T
 //     fragments are two transposed reads (ds_read_b64_tr_b16) each, so V
 //     needs no transposing copy. Streaming mode, which gathers rows from the
-//     ring and the chunk per lane, stages through registers instead (K rows
-//     padded by 16 bytes, V transposed on the way to LDS);
+//     ring and the chunk per lane, and the 4-bit mode, which decodes codes,
+//     stage through registers instead (K rows padded by 16 bytes, V
+//     transposed on the way to LDS);
 //   * the next tile's loads are in flight while the current tile is
-//     computed; query tiles are launched longest-first (causal imbalance).
+//     computed; query tiles are launched longest-first (causal imbalance);
+//   * output rows leave through LDS as whole rows (coalesced stores).
 #include <mutex>
 #include <type_traits>
 
