@@ -169,3 +169,40 @@ def test_prefill_int4_llama3_gqa_4k_sampled():
     mask = (1, 0, 1, 1, 0, 0, 1, 0)
     _run(32, 8, 128, mask, [2048, 2048], kv_dtype="fp16", retrieval_dtype="int4", seed=9900,
          sample_rows=64)
+
+
+@pytest.mark.parametrize("kv_dtype,retrieval_dtype", [("fp16", "int4"), ("bf16", "int4"),
+                                                      ("fp16", "fp16")])
+def test_prefill_quant_batch2(kv_dtype, retrieval_dtype):
+    """Batch-wide prefill of two sequences (each against its own oracle):
+    every (sequence, head) finds its own cache rows, codes and scale words."""
+    Hq, Hkv, D = 16, 4, 128
+    mask = (0, 1, 1, 0)
+    G = Hq // Hkv
+    chunks = [90, 170]
+    say(f"case: batch 2 {kv_dtype}/{retrieval_dtype} chunks={chunks}")
+    lay, orcs, r = _layer(Hq, Hkv, D, mask, sum(chunks) + 1, D ** -0.5, kv_dtype,
+                          retrieval_dtype, batch=2)
+    rq = np.array([mask[h // G] for h in range(Hq)], bool)
+    data = [_case(9950 + b, sum(chunks) + 1, Hq, Hkv, D, kv_dtype) for b in range(2)]
+    tdt = _TDT[kv_dtype]
+    a = 0
+    for c in chunks:
+        q = torch.stack([r.q(to_dev(data[b][0][a:a + c])) for b in range(2)])
+        k = torch.stack([r.kv(to_dev(data[b][1][a:a + c], tdt)) for b in range(2)])
+        v = torch.stack([r.kv(to_dev(data[b][2][a:a + c], tdt)) for b in range(2)])
+        out = lay.prefill_chunk(q, k, v)
+        for b in range(2):
+            ref = orcs[b].prefill_chunk(*(x[a:a + c] for x in data[b]))
+            assert_blocks_close(r.out(out[b]).float().cpu().numpy(), ref, rq,
+                                f"seq {b} chunk@{a}+{c}", head_axis=1)
+        a += c
+    # one decode step of both sequences after the prefill
+    t = a
+    out = lay.decode(torch.stack([r.q(to_dev(data[b][0][t]))[None] for b in range(2)]),
+                     torch.stack([r.kv(to_dev(data[b][1][t], tdt))[None] for b in range(2)]),
+                     torch.stack([r.kv(to_dev(data[b][2][t], tdt))[None] for b in range(2)]))
+    for b in range(2):
+        ref = orcs[b].decode(*(x[t] for x in data[b]))
+        assert_blocks_close(r.out(out[b, 0]).float().cpu().numpy(), ref, rq, f"seq {b} decode",
+                            head_axis=0)
