@@ -51,16 +51,21 @@ struct DecodeArgs {
   int nseq[kMaxRaggedBatch];  // position of the new token per sequence
 };
 
-// Waves per block and tiles per wave held in registers (measured on the
+// Waves per block and tiles per wave held in registers. One or two query
+// heads per KV head: 4 waves with 2 tiles of 16 rows (measured on the
 // Llama-2 layer: 8 or 16 waves per block, or 3 or 4 tiles in flight per wave,
-// were slower than 4 waves with 2 tiles of 16 rows).
-constexpr int kDecodeWaves = 4;
+// were slower). Four or more: the G dot products and accumulations per row
+// make the loop VALU-bound, and 8 waves (two per SIMD) overlap one wave's
+// arithmetic with another's loads (3 tiles in flight instead: no gain); at
+// head_dim 64 the 8-wave form spills, so it keeps 4.
+template <int D, int G>
+constexpr int decode_waves() { return G >= 4 && D == 128 ? 8 : 4; }
 constexpr int kDecodePrefetch = 2;
 
 template <int D, int G, typename Tag>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((64 * decode_waves<D, G>())) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;
-  constexpr int NW = kDecodeWaves;
+  constexpr int NW = decode_waves<D, G>();
   constexpr int PF = kDecodePrefetch;
   __shared__ BlockRed<D, G, NW> red;
   const int b = blockIdx.y;
@@ -173,7 +178,7 @@ static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int split_tokens, 
   a.n_split = a.Hr > 0 ? (int)((rows + split_tokens - 1) / split_tokens) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
-  decode_kernel<D, G, Tag><<<grid, 64 * kDecodeWaves, 0, s>>>(a);
+  decode_kernel<D, G, Tag><<<grid, 64 * decode_waves<D, G>(), 0, s>>>(a);
   return hipGetLastError();
 }
 
