@@ -332,6 +332,9 @@ struct alignas(16) BlockRed {
 };
 
 template <int D, int G, int NW>
+__device__ __forceinline__ void block_merge_lds(BlockRed<D, G, NW>& red);
+
+template <int D, int G, int NW>
 __device__ __forceinline__ void block_merge(BlockRed<D, G, NW>& red, const WaveState<G>& st) {
   constexpr int LPR = D / 8;
   const int lane = threadIdx.x & 63;
@@ -347,6 +350,14 @@ __device__ __forceinline__ void block_merge(BlockRed<D, G, NW>& red, const WaveS
       }
     }
   }
+  block_merge_lds<D, G, NW>(red);
+}
+
+// The reduction part of block_merge, for callers that wrote each wave's (m, l,
+// acc) into red themselves (m in the log2 domain, -inf for a wave without
+// rows).
+template <int D, int G, int NW>
+__device__ __forceinline__ void block_merge_lds(BlockRed<D, G, NW>& red) {
   __syncthreads();
   if (threadIdx.x < G) {
     int g = threadIdx.x;

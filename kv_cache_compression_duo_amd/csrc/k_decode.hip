@@ -23,6 +23,7 @@
 // block, so no block reads memory another block writes.
 #include "device_common.hpp"
 #include "decode_common.hpp"
+#include "decode_mma.hpp"
 #include "duo_internal.hpp"
 #include "split_merge.hpp"
 
@@ -51,23 +52,30 @@ struct DecodeArgs {
   int nseq[kMaxRaggedBatch];  // position of the new token per sequence
 };
 
-// Waves per block and tiles per wave held in registers. One or two query
-// heads per KV head: 4 waves with 2 tiles of 16 rows (measured on the
-// Llama-2 layer: 8 or 16 waves per block, or 3 or 4 tiles in flight per wave,
-// were slower). Four or more: the G dot products and accumulations per row
-// make the loop VALU-bound, and 8 waves (two per SIMD) overlap one wave's
-// arithmetic with another's loads (3 tiles in flight instead: no gain); at
-// head_dim 64 the 8-wave form spills, so it keeps 4.
-template <int D, int G>
-constexpr int decode_waves() { return G >= 4 && D == 128 ? 8 : 4; }
+// Retrieval heads of layers with four or more query heads per KV head attend
+// on the matrix cores (decode_mma.hpp): on the VALU the G dot products and
+// accumulations per row made that loop arithmetic-bound. One or two heads
+// per KV head keep the VALU loop, which streams at the HBM rate.
+template <int G>
+constexpr bool decode_on_mfma() { return G >= 4; }
+// Waves per block and tiles per wave held in registers (VALU loop): 4 waves
+// with 2 tiles of 16 rows (measured on the Llama-2 layer: 8 or 16 waves per
+// block, or 3 or 4 tiles in flight per wave, were slower). The matrix-core
+// path keeps 4 waves too: each holds two 32-row K/V stages in LDS.
+constexpr int kDecodeWaves = 4;
 constexpr int kDecodePrefetch = 2;
 
 template <int D, int G, typename Tag>
-__global__ __launch_bounds__((64 * decode_waves<D, G>())) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;
-  constexpr int NW = decode_waves<D, G>();
+  constexpr int NW = kDecodeWaves;
   constexpr int PF = kDecodePrefetch;
+  constexpr bool kMma = decode_on_mfma<G>();
   __shared__ BlockRed<D, G, NW> red;
+  // the matrix-core path's per-wave stages (four arrays, so the compiler's
+  // tracking of the direct loads tells the stage read from the stage filled)
+  constexpr int MS = kMma ? NW * kMmaRows * D : 8;
+  __shared__ __align__(16) uint16_t mk0[MS], mk1[MS], mv0[MS], mv1[MS];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int lc = lane % LPR;
@@ -106,24 +114,34 @@ __global__ __launch_bounds__((64 * decode_waves<D, G>())) void decode_kernel(Dec
     // cache rows [r0, min(r1, n)); the split holding position n adds the
     // new token from its input; splits past n are empty (m = -inf)
     const bool has_new = r0 <= n && r1 == n + 1;
-    QFrag<G> qfrag;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const u32x4 raw = ld16(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + lc * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qfrag.w[g][i] = word_of(raw, i);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qfrag.f[g][c] = qf[g][c];
-    }
     const uint32_t slab_bytes = (uint32_t)((a.cap + kDecodePadRows) * D * 2);
-    attend_cache<D, G, Tag, NW, PF>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc, slab_bytes,
-                                r0, has_new ? n : r1, knew, vnew, has_new);
+    if constexpr (kMma) {
+      const int wo = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kMmaRows * D;
+      attend_cache_mma<D, G, Tag, NW>(red, a.q + ((int64_t)b * a.Hq + kvh * G) * D, a.qscale, kc,
+                                      vc, slab_bytes, r0, has_new ? n : r1, knew, vnew, has_new,
+                                      mk0 + wo, mk1 + wo, mv0 + wo, mv1 + wo);
+    } else {
+      QFrag<G> qfrag;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const u32x4 raw = ld16(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + lc * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qfrag.w[g][i] = word_of(raw, i);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qfrag.f[g][c] = qf[g][c];
+      }
+      attend_cache<D, G, Tag, NW, PF>(st, qfrag, Tag::is_bf16 ? a.qscale : 1.0f, kc, vc,
+                                      slab_bytes, r0, has_new ? n : r1, knew, vnew, has_new);
+    }
     // the new token's cache row (read by no block of this launch)
     if (split == 0 && threadIdx.x < LPR) {
       st16(a.kc + (hb * a.cap + n) * D + threadIdx.x * 8, ld16(knew + threadIdx.x * 8));
       st16(a.vc + (hb * a.cap + n) * D + threadIdx.x * 8, ld16(vnew + threadIdx.x * 8));
     }
-    block_merge<D, G, NW>(red, st);
+    if constexpr (kMma)
+      block_merge_lds<D, G, NW>(red);
+    else
+      block_merge<D, G, NW>(red, st);
     // Publish this split's partial state. The partials are written and read
     // with device-coherent accesses and the writes complete before the arrival
     // count is bumped, so no cache-wide writeback or invalidate is needed on
@@ -178,7 +196,7 @@ static hipError_t launch_t(DecodeArgs a, int B, int64_t rows, int split_tokens, 
   a.n_split = a.Hr > 0 ? (int)((rows + split_tokens - 1) / split_tokens) : 0;
   if (a.n_split > max_split) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.Hr * a.n_split + a.Hs), (unsigned)B);
-  decode_kernel<D, G, Tag><<<grid, 64 * decode_waves<D, G>(), 0, s>>>(a);
+  decode_kernel<D, G, Tag><<<grid, 64 * kDecodeWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 

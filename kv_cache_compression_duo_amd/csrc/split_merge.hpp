@@ -80,86 +80,87 @@ struct MergeLds {
   float4 o[NT];
 };
 
-// Merge the n_split partials into out row g at out + g*D (bf16). Thread
-// (part, c4) folds the splits part, part + P, ... for channels 4*c4..4*c4+3:
-// each split costs it one 16-byte acc load and one 8-byte (m, l) load, issued
-// UN splits at a time with clamped (always valid) indices so that a batch is
-// one memory round trip; entries past the last split get weight 0. The P
-// parts of each channel quadruple are then folded through LDS.
+// Merge the n_split partials into out rows g = 0..G-1 at out + g*D (bf16), all
+// heads in one pass. Thread (part, g, c4) folds the splits part, part + P, ...
+// of head g for channels 4*c4..4*c4+3 (P = NT / (G * D/4) parts): each split
+// costs it one 16-byte acc load and one 8-byte (m, l) load, issued UN splits
+// at a time with clamped (always valid) indices so that a batch is one memory
+// round trip (16 to 64 splits per round trip); entries past
+// the last split get weight 0. The P parts of each (head, channel quadruple)
+// are then folded through LDS.
 template <int D, int G, int NT>
 __device__ void merge_splits(MergeLds<NT>& s, const PartialView& pv, int max_split, int n_split,
                              uint16_t* __restrict__ out) {
-  constexpr int Q = D / 4;   // 16-byte columns of a partial row
-  constexpr int P = NT / Q;  // splits folded in parallel
-  constexpr int UN = 4;
-  static_assert(NT % Q == 0, "whole partial rows per pass");
+  constexpr int Q = D / 4;     // 16-byte columns of a partial row
+  constexpr int GQ = G * Q;    // (head, column) pairs
+  static_assert(NT % GQ == 0, "whole partial rows of every head per pass");
+  constexpr int P = NT / GQ;   // splits folded in parallel per pair
+  constexpr int UN = P >= 8 ? 4 : (32 / P < 16 ? 32 / P : 16);
   const int t = threadIdx.x;
-  const int c4 = t % Q, part = t / Q;
-  for (int g = 0; g < G; ++g) {
-    float m = -INFINITY, l = 0.0f;
-    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int sp0 = part; sp0 < n_split; sp0 += UN * P) {
-      float2 mlv[UN];
-      float4 av[UN];
+  const int c4 = t % Q, g = (t / Q) % G, part = t / GQ;
+  float m = -INFINITY, l = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int sp0 = part; sp0 < n_split; sp0 += UN * P) {
+    float2 mlv[UN];
+    float4 av[UN];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int sp = sp0 + u * P < n_split ? sp0 + u * P : n_split - 1;
-        const int row = g * max_split + sp;
-        mlv[u] = ld_agent8(pv.ml, (uint32_t)(row * 8));
-        av[u] = ld_agent16(pv.acc, (uint32_t)((row * D + 4 * c4) * 4));
-      }
-      float mx = m;
-#pragma unroll
-      for (int u = 0; u < UN; ++u)
-        if (sp0 + u * P < n_split) mx = fmaxf(mx, mlv[u].x);
-      // a split with no row (m = -inf: past a shorter sequence's end) has
-      // weight 0; guard -inf - -inf while every split so far is empty
-      const float c = m == -INFINITY ? 0.0f : fast_exp2(m - mx);
-      l *= c;
-      o.x *= c;
-      o.y *= c;
-      o.z *= c;
-      o.w *= c;
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const bool use = sp0 + u * P < n_split && mlv[u].x != -INFINITY;
-        const float w = use ? fast_exp2(mlv[u].x - mx) : 0.0f;
-        l = fmaf(mlv[u].y, w, l);
-        o.x = fmaf(av[u].x, w, o.x);
-        o.y = fmaf(av[u].y, w, o.y);
-        o.z = fmaf(av[u].z, w, o.z);
-        o.w = fmaf(av[u].w, w, o.w);
-      }
-      m = mx;
+    for (int u = 0; u < UN; ++u) {
+      const int sp = sp0 + u * P < n_split ? sp0 + u * P : n_split - 1;
+      const int row = g * max_split + sp;
+      mlv[u] = ld_agent8(pv.ml, (uint32_t)(row * 8));
+      av[u] = ld_agent16(pv.acc, (uint32_t)((row * D + 4 * c4) * 4));
     }
-    s.m[t] = m;
-    s.l[t] = l;
-    s.o[t] = o;
-    __syncthreads();
-    if (t < Q) {
-      float M = s.m[t];
+    float mx = m;
 #pragma unroll
-      for (int p = 1; p < P; ++p) M = fmaxf(M, s.m[p * Q + t]);
-      float L = 0.0f;
-      float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int u = 0; u < UN; ++u)
+      if (sp0 + u * P < n_split) mx = fmaxf(mx, mlv[u].x);
+    // a split with no row (m = -inf: past a shorter sequence's end) has
+    // weight 0; guard -inf - -inf while every split so far is empty
+    const float c = m == -INFINITY ? 0.0f : fast_exp2(m - mx);
+    l *= c;
+    o.x *= c;
+    o.y *= c;
+    o.z *= c;
+    o.w *= c;
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float mp = s.m[p * Q + t];
-        const float w = mp == -INFINITY ? 0.0f : fast_exp2(mp - M);
-        const float4 op = s.o[p * Q + t];
-        L = fmaf(s.l[p * Q + t], w, L);
-        O.x = fmaf(op.x, w, O.x);
-        O.y = fmaf(op.y, w, O.y);
-        O.z = fmaf(op.z, w, O.z);
-        O.w = fmaf(op.w, w, O.w);
-      }
-      uint2 pk;
-      pk.x = pack_bf16x2(O.x / L, O.y / L);
-      pk.y = pack_bf16x2(O.z / L, O.w / L);
-      *reinterpret_cast<uint2*>(out + (int64_t)g * D + 4 * t) = pk;
+    for (int u = 0; u < UN; ++u) {
+      const bool use = sp0 + u * P < n_split && mlv[u].x != -INFINITY;
+      const float w = use ? fast_exp2(mlv[u].x - mx) : 0.0f;
+      l = fmaf(mlv[u].y, w, l);
+      o.x = fmaf(av[u].x, w, o.x);
+      o.y = fmaf(av[u].y, w, o.y);
+      o.z = fmaf(av[u].z, w, o.z);
+      o.w = fmaf(av[u].w, w, o.w);
     }
-    __syncthreads();
+    m = mx;
   }
+  s.m[t] = m;
+  s.l[t] = l;
+  s.o[t] = o;
+  __syncthreads();
+  if (t < GQ) {
+    float M = s.m[t];
+#pragma unroll
+    for (int p = 1; p < P; ++p) M = fmaxf(M, s.m[p * GQ + t]);
+    float L = 0.0f;
+    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float mp = s.m[p * GQ + t];
+      const float w = mp == -INFINITY ? 0.0f : fast_exp2(mp - M);
+      const float4 op = s.o[p * GQ + t];
+      L = fmaf(s.l[p * GQ + t], w, L);
+      O.x = fmaf(op.x, w, O.x);
+      O.y = fmaf(op.y, w, O.y);
+      O.z = fmaf(op.z, w, O.z);
+      O.w = fmaf(op.w, w, O.w);
+    }
+    uint2 pk;
+    pk.x = pack_bf16x2(O.x / L, O.y / L);
+    pk.y = pack_bf16x2(O.z / L, O.w / L);
+    *reinterpret_cast<uint2*>(out + (int64_t)g * D + 4 * c4) = pk;
+  }
+  __syncthreads();
 }
 
 }  // namespace duo
