@@ -33,7 +33,7 @@ namespace duo {
 constexpr int kMmaRows = 32;
 
 // Attend the G query heads whose rows start at q_heads ([G][D] bf16) over
-// cache rows [r0, r1) of kc/vc (slab_bytes readable from each, below 2^31),
+// cache rows [r0, r1) of kc/vc (head bases; every row offset below 2^31 bytes),
 // plus the new token (knew, vnew) in wave 0 when with_new. k0/k1/v0/v1 are
 // this wave's two K and two V stages of kMmaRows * D elements each; they must
 // point into four distinct __shared__ arrays. c2 = softmax scale * log2(e).
@@ -43,7 +43,7 @@ template <int D, int G, typename Tag, int NW>
 __device__ __forceinline__ void attend_cache_mma(BlockRed<D, G, NW>& red,
                                                  const uint16_t* q_heads, float c2,
                                                  const uint16_t* kc, const uint16_t* vc,
-                                                 uint32_t slab_bytes, int r0, int r1,
+                                                 int r0, int r1,
                                                  const uint16_t* knew, const uint16_t* vnew,
                                                  bool with_new, uint16_t* k0, uint16_t* k1,
                                                  uint16_t* v0, uint16_t* v1) {
@@ -94,27 +94,26 @@ __device__ __forceinline__ void attend_cache_mma(BlockRed<D, G, NW>& red,
   // ---- direct loads of one 32-row tile into a stage ------------------------------
   // Load j covers tile rows j*RPI .. + RPI - 1; lane i writes LDS slot i of the
   // load's 1 KB (row j*RPI + i/SPR, slot i%SPR) and so fetches the source chunk
-  // that belongs there. A tile wholly inside [r0, r1) takes its row offset as
-  // the scalar offset (no address VALU); a tile reaching past r1 clamps each
-  // lane's row to r1 - 1 (finite values; the mask removes those keys).
-  const __amdgpu_buffer_rsrc_t krs = wave_rsrc(kc, slab_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(vc, slab_bytes);
+  // that belongs there (lane offsets precomputed per load). The tile's rows up
+  // to r1 are one buffer resource built in scalar registers: lanes past r1 are
+  // out of its range and write zeros to LDS (keys masked, values finite), so no
+  // address arithmetic runs per tile and no load leaves the head's rows.
   const int rl = lane / SPR, pos = lane % SPR;
-  uint32_t kl[JK];
+  uint32_t kvo[NL], vvo[NL];
 #pragma unroll
-  for (int jm = 0; jm < JK; ++jm)
-    kl[jm] = (uint32_t)(rl * RB + 16 * (pos ^ ksw(jm * RPI + rl)));
-  const uint32_t vl = (uint32_t)(rl * RB + 16 * (2 * ((pos >> 1) ^ vsw(rl)) + (pos & 1)));
+  for (int j = 0; j < NL; ++j) {
+    kvo[j] = (uint32_t)(j * 1024 + rl * RB + 16 * (pos ^ ksw(j * RPI + rl)));
+    vvo[j] = (uint32_t)(j * 1024 + rl * RB + 16 * (2 * ((pos >> 1) ^ vsw(rl)) + (pos & 1)));
+  }
   auto dma = [&](int t, uint16_t* ks, uint16_t* vs) {
+    const int nrow = r1 - t < 0 ? 0 : r1 - t < kMmaRows ? r1 - t : kMmaRows;  // wave-uniform
+    const uint32_t nbytes = (uint32_t)(nrow * RB);
+    const __amdgpu_buffer_rsrc_t krs = wave_rsrc(kc + (int64_t)t * D, nbytes);
+    const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(vc + (int64_t)t * D, nbytes);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      int row = t + j * RPI + rl;
-      row = row < r1 - 1 ? row : r1 - 1;
-      const uint32_t ro = (uint32_t)row * (uint32_t)RB - (uint32_t)(rl * RB);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(ks + j * 512), 16,
-                                               (int)(ro + kl[j % JK]), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds_ptr(vs + j * 512), 16, (int)(ro + vl),
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(ks + j * 512), 16, (int)kvo[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds_ptr(vs + j * 512), 16, (int)vvo[j], 0, 0, 0);
     }
   };
 
@@ -154,8 +153,13 @@ __device__ __forceinline__ void attend_cache_mma(BlockRed<D, G, NW>& red,
     float tm = st[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) tm = fmaxf(tm, st[j]);
-    // lanes l and l + 32 hold the two halves of a head's keys
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    // lanes l and l + 32 hold the two halves of a head's keys: one
+    // v_permlane32_swap gives every lane its partner's maximum
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm),
+                                                       false, false);
+      tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     if (__ballot(tm > m + lazy) != 0) {
       // every tile holds a key below r1, so mn is finite; m = -inf gives 0
       const float mn = fmaxf(m, tm);

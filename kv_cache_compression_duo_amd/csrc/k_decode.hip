@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     if constexpr (kMma) {
       const int wo = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kMmaRows * D;
       attend_cache_mma<D, G, Tag, NW>(red, a.q + ((int64_t)b * a.Hq + kvh * G) * D, a.qscale, kc,
-                                      vc, slab_bytes, r0, has_new ? n : r1, knew, vnew, has_new,
+                                      vc, r0, has_new ? n : r1, knew, vnew, has_new,
                                       mk0 + wo, mk1 + wo, mv0 + wo, mv1 + wo);
     } else {
       QFrag<G> qfrag;
