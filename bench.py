@@ -110,8 +110,8 @@ TRAFFIC = {
     "decode": dict(
         kernel="decode_kernel<128, 1, duo::Bf16Tag>", workload="llama2_7b_decode_32k",
         json=os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_32k_traffic.json"),
-        sources=["k_decode.hip", "decode_common.hpp", "split_merge.hpp", "device_common.hpp",
-                 "duo_api.cpp", "duo_internal.hpp"]),
+        sources=["k_decode.hip", "decode_common.hpp", "decode_mma.hpp", "mfma_common.hpp",
+                 "split_merge.hpp", "device_common.hpp", "duo_api.cpp", "duo_internal.hpp"]),
     "int4": dict(
         kernel="decode_int4_kernel<128, 4, duo::Fp16Tag>", workload="llama3_8b_int4_decode_1m",
         json=os.path.join(ROOT, "profiles", "decode_int4_kernel_llama3_8b_1m_traffic.json"),
@@ -344,6 +344,58 @@ def bench_decode_llama2(args, dev):
                      "kernel": "duo::decode_kernel<128, 1, duo::Bf16Tag>",
                      "avg_launch_us": ms_step * 1e3},
     }
+
+
+def bench_decode_gqa(args, dev):
+    """Opt-in (--only gqa): the 16-bit decode of a Llama-3-8B-shaped layer (32
+    query / 8 KV heads, head_dim 128, 32768-token context, 8 layers cycled) with
+    4 and with 8 retrieval KV heads -- four query heads per KV head, the
+    matrix-core decode loop. Not a headline workload."""
+    import torch
+    import kv_cache_compression_duo_amd as duo
+    from duo_synth import device_normal
+
+    Hq, Hkv, D, ctx, L, S, R = 32, 8, 128, 32768, args.layers, 16, 64
+    total = args.warmup + args.steps
+    per_layer = (total + L - 1) // L
+    res = {}
+    for Hr in (4, 8):
+        layers = []
+        for li in range(L):
+            lay = duo.DuoLayer(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_retrieval_kv_heads=Hr,
+                               capacity=ctx + per_layer, softmax_scale=D ** -0.5, sink=S,
+                               recent=R, device=dev)
+            for a in range(0, ctx, 8192):
+                lay.append_kv(device_normal((1, 8192, Hkv, D), 7000 + li * 100 + a // 8192, dev,
+                                            torch.bfloat16),
+                              device_normal((1, 8192, Hkv, D), 9000 + li * 100 + a // 8192, dev,
+                                            torch.bfloat16))
+            layers.append(lay)
+        q = device_normal((total, 1, 1, Hq, D), 11, dev, torch.bfloat16)
+        kn = device_normal((total, 1, 1, Hkv, D), 12, dev, torch.bfloat16)
+        vn = device_normal((total, 1, 1, Hkv, D), 13, dev, torch.bfloat16)
+        out = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+        for s in range(args.warmup):
+            layers[s % L].decode(q[s], kn[s], vn[s], out)
+        torch.cuda.synchronize()
+        n_before = [lay.n_tokens for lay in layers]
+        nbytes = sum(decode_step_bytes(n_before[(args.warmup + i) % L] + i // L, Hr, Hkv - Hr, Hq,
+                                       Hkv, D, S + R, D * 2 * 2) for i in range(args.steps))
+        t0, t1 = _events(torch)
+        t0.record()
+        for i in range(args.steps):
+            s = args.warmup + i
+            layers[s % L].decode(q[s], kn[s], vn[s], out)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[f"retrieval_kv_heads_{Hr}"] = {"us_per_step": ms / args.steps * 1e3,
+                                           "bytes_per_step": nbytes / args.steps, "kv_gbs": gbs,
+                                           "hbm_frac": gbs / HBM_PEAK_GBS}
+        del layers
+    res["kernel"] = "duo::decode_kernel<128, 4, duo::Bf16Tag>"
+    return res
 
 
 def bench_mha8(args, dev):
@@ -620,7 +672,9 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of: decode,mha8,prefill,mixed,grad,int4")
+    ap.add_argument("--only", default="",
+                    help="comma list of: decode,mha8,prefill,mixed,grad,int4 (default: all), "
+                         "and the opt-in gqa")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the counter runs measure")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -675,6 +729,10 @@ def main():
         if want(name):
             work[key] = fn(args, dev)
             print(f"# {key}: {json.dumps(work[key])}", file=sys.stderr, flush=True)
+    if "gqa" in only:
+        work["llama3_8b_decode_32k_gqa"] = bench_decode_gqa(args, dev)
+        print(f"# llama3_8b_decode_32k_gqa: {json.dumps(work['llama3_8b_decode_32k_gqa'])}",
+              file=sys.stderr, flush=True)
     line["workloads"] = work
     if want("decode") and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget)
