@@ -200,8 +200,9 @@ __device__ __forceinline__ void attend_cache_mma(BlockRed<D, G, NW>& red,
   };
 
   // ---- the wave's tiles: two stages, the next tile's loads in flight ----------------
-  // The prefetch is issued even past the range (rows clamp to r1 - 1, never
-  // computed), so both paths of every step issue the same loads.
+  // The prefetch is issued even past the range (its resource is empty, so the
+  // stage fills with zeros and is never computed): every step issues the same
+  // loads, and the compiler's wait before a stage's reads covers that stage only.
   constexpr int stride = kMmaRows * NW;
   int t = r0 + kMmaRows * wave;
   if (t < r1) {
