@@ -51,6 +51,11 @@ def _load():
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m kv_cache_compression_duo_amd.build` "
             "(there is no fallback path)")
+    # torch's HIP runtime has to be in the process before the library is opened: the
+    # library's libamdhip64 dependency then resolves to that same runtime, which owns the
+    # device memory and streams torch hands over. Opened first, the library would pull in
+    # a second HIP runtime, and that second copy finds no device next to torch's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "duo_layer_layout": (c_int, [POINTER(LayerDesc), POINTER(Layout)]),

@@ -273,3 +273,18 @@ def test_binding_has_no_host_path():
     with pytest.raises(ValueError, match="not a GPU"):
         duo.DuoLayer(n_q_heads=2, n_kv_heads=2, head_dim=64, n_retrieval_kv_heads=1,
                      capacity=16, softmax_scale=0.125, device="cpu")
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not load a second HIP runtime:
+    the library has to share torch's, which owns the device memory and streams
+    it is handed (a second runtime in the process sees no device)."""
+    import ast
+    import subprocess
+    import sys
+    code = ("import kv_cache_compression_duo_amd, torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300, check=True).stdout
+    paths = ast.literal_eval(out.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
