@@ -192,6 +192,15 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // with direct global->LDS loads (see below); streaming mode gathers rows
   // per lane, and the 4-bit mode dequantises codes, through registers.
   constexpr bool kDma = !kStream && !kI4;
+  // Retrieval modes over 16-bit caches keep the softmax reference in the
+  // product itself: q is scaled by scale * log2(e) once per block and each
+  // QK accumulation starts from a register block holding -m, so a product
+  // already is the exp2 argument (no FMA per score). The other modes stay
+  // with raw scores: the streaming form has no 16 registers to spare, the
+  // 4-bit form few, and the two-phase forms keep q as given (the gate
+  // gradient's error bound counts the rounding of P as its only
+  // approximation; rounding q * scale * log2(e) would add a second one).
+  constexpr bool kRel = kCache && !kI4;
   constexpr int KROW = kDma ? D : KPAD;  // K tile row stride in LDS (elements)
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
   // written to the other, so one barrier per tile suffices. The stages are
@@ -275,6 +284,11 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
         }
       } else {
         qf[ks] = as_bf16x8(w);
+      }
+      if constexpr (kRel) {
+        // q * scale * log2(e), rounded once to the operand type
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[ks][i] = (Elem)((float)qf[ks][i] * a.scale_log2);
       }
     }
   }
@@ -532,6 +546,13 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   for (int db = 0; db < DB; ++db) o_f[db] = f32x16{};
   float m_f = -INFINITY, l_f = 0.0f;
   float mc_f = 0.0f;  // m_f * scale_log2, or 0 while m_f = -inf (no allowed key yet)
+  // kRel: mc_f is the reference in exp2 units (0 while the lane has seen no
+  // allowed key, unset), and neg_m holds -mc_f in each of its 16 elements:
+  // the QK accumulators start from it. Kept opaque so the compiler holds the
+  // block in registers rather than rebuilding it from mc_f on every tile.
+  bool unset = true;
+  f32x16 neg_m{};
+  if constexpr (kRel) asm volatile("" : "+v"(neg_m));
   __shared__ uint32_t lam_lds[kMixed ? NW * DB * 8 * 64 : 1];
   auto lam_at = [&](int db, int i) -> uint32_t& {
     return lam_lds[((wave * DB + db) * 8 + i) * 64 + lane];
@@ -596,12 +617,49 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       mc = mn == -INFINITY ? 0.0f : mn * c2;
     }
   };
+  // kRel form: sc already holds scale_log2 * score - mc (the QK product
+  // started from neg_m), so the lazy test compares with 8 directly. On a
+  // rescale a lane moves its reference up by delta = max(tm, 0) (an unset
+  // lane to its first tile maximum) and takes delta off this tile's values.
+  auto softmax_rescale_rel = [&](f32x16 (&sc)[2], float& l, f32x16 (&O)[DB]) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sc[kb][j]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm),
+                                                       false, false);
+      asm("v_max_f32 %0, %1, %2" : "=v"(tm) : "v"(__uint_as_float(sw[0])),
+          "v"(__uint_as_float(sw[1])));
+    }
+    // an unset lane with a finite maximum always rescales
+    if (__ballot((tm > 8.0f) | (unset & (tm != -INFINITY))) != 0) {
+      // unset: l = 0 and O = 0, so the factor only has to be finite; a lane
+      // still without an allowed key (tm = -inf) stays unset with delta 0
+      const float delta = unset ? (tm == -INFINITY ? 0.0f : tm) : fmaxf(tm, 0.0f);
+      const float corr = unset ? 1.0f : fast_exp2(-delta);
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) O[db] *= corr;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[kb][j] -= delta;
+      mc_f += delta;
+      unset = unset & (tm == -INFINITY);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) neg_m[j] = -mc_f;
+      asm volatile("" : "+v"(neg_m));
+    }
+  };
   auto softmax_weights = [&](const f32x16 (&sc)[2], float mc, float& l, E8 (&pb)[4]) {
     float p[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[kb][j] = fast_exp2(fmaf(sc[kb][j], c2, -mc));
+      for (int j = 0; j < 16; ++j)
+        p[kb][j] = kRel ? fast_exp2(sc[kb][j]) : fast_exp2(fmaf(sc[kb][j], c2, -mc));
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -618,9 +676,12 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
       }
     l = ls0 + ls1;
   };
-  auto softmax_update = [&](const f32x16 (&sc)[2], float& m, float& mc, float& l,
+  auto softmax_update = [&](f32x16 (&sc)[2], float& m, float& mc, float& l,
                             f32x16 (&O)[DB], E8 (&pb)[4]) {
-    softmax_rescale(sc, m, mc, l, O);
+    if constexpr (kRel)
+      softmax_rescale_rel(sc, l, O);
+    else
+      softmax_rescale(sc, m, mc, l, O);
     softmax_weights(sc, mc, l, pb);
   };
   // V^T fragment of lane (q32, h2) for slice s and d-block db: channel
@@ -689,8 +750,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
     if constexpr (kMixed) asm volatile("" : "+v"(k_off[ks_]));
   }
   auto qk = [&](const uint16_t* ks, f32x16 (&st)[2]) {
-    st[0] = f32x16{};
-    st[1] = f32x16{};
+    st[0] = kRel ? neg_m : f32x16{};
+    st[1] = kRel ? neg_m : f32x16{};
     E8 ak0[KS], ak1[KS];
     if constexpr (kDma) {
       const char* kb = reinterpret_cast<const char*>(ks);
