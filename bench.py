@@ -266,6 +266,19 @@ def kernel_summary(trace_dir, group=8):
         passes = [sum(d[i:i + group]) / 1000 for i in range(0, len(d) - group + 1, group)]
         print(f"`{name}`: totals of successive groups of {group} dispatches (ms): "
               + ", ".join(f"{x:.3f}" for x in passes))
+    # the headline decode runs twice per bench: its steps cycling over several
+    # layers, then the same number of steps on one layer (warm); each leg
+    # starts with `group` warm-up steps
+    for name, v in sorted(per.items()):
+        if "decode_kernel<128, 1," not in name:
+            continue
+        d = [x for _, x in sorted(v)]
+        h = len(d) // 2
+        legs = [d[group:h], d[h + group:]]
+        if all(legs):
+            print(f"`{name}`: average of the timed dispatches of the cycled-layer leg "
+                  f"{sum(legs[0]) / len(legs[0]):.2f} us ({len(legs[0])}), of the one-layer "
+                  f"(warm) leg {sum(legs[1]) / len(legs[1]):.2f} us ({len(legs[1])})")
 
 
 def counter_summary(*run_dirs):
