@@ -197,10 +197,8 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // QK accumulation starts from a register block holding -m, so a product
   // already is the exp2 argument (no FMA per score). The other modes stay
   // with raw scores: the streaming form has no 16 registers to spare, the
-  // 4-bit form few, and the gate gradient keeps q as given (its error bound
-  // counts the rounding of P as the only approximation; rounding
-  // q * scale * log2(e) would add a second one).
-  constexpr bool kRel = (kCache && !kI4) || kMixed;
+  // 4-bit form few.
+  constexpr bool kRel = (kCache && !kI4) || kTwoPhase;
   constexpr int KROW = kDma ? D : KPAD;  // K tile row stride in LDS (elements)
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
   // written to the other, so one barrier per tile suffices. The stages are

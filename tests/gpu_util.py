@@ -92,7 +92,13 @@ def grad_tolerance(q, k, v, dout, scale, S, R, block=0):
     within 6 * 2^-9 * sqrt(sum (w_tj * dout_t . (v_j - o_t))^2) over both
     attentions (exceeded with probability below 1e-7); 1e-5 of
     sum |dout * o| is added for fp32 accumulation. ``block`` > 0 takes the
-    streaming mask block-sparse (64-token blocks in the kernel)."""
+    streaming mask block-sparse (64-token blocks in the kernel).
+
+    The kernel also rounds q * scale * log2(e) once to bf16 (relative error
+    eps_td <= 2^-9 per element), one query for both attentions. To first order
+    that moves the gradient by sum_td eps_td * a_td with
+    a_td = scale * q_td * sum_j (w^full_tj dv^full_tj - w^lam_tj dv^lam_tj) k_jd,
+    dv_tj = dout_t . (v_j - o_t); these terms join the same Hoeffding sum."""
     q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
     T, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -110,6 +116,7 @@ def grad_tolerance(q, k, v, dout, scale, S, R, block=0):
     for h in range(Hq):
         kv = h // G
         s = scale * q[:, h] @ k[:, kv].T
+        wdv = []
         for allowed in (causal, lam):
             z = np.where(allowed, s, -np.inf)
             z -= z.max(axis=1, keepdims=True)
@@ -119,6 +126,9 @@ def grad_tolerance(q, k, v, dout, scale, S, R, block=0):
             dv = dout[:, h] @ v[:, kv].T - np.sum(dout[:, h] * o, axis=1, keepdims=True)
             var[kv] += np.sum((w * dv) ** 2)
             mass[kv] += np.sum(np.abs(dout[:, h] * o))
+            wdv.append(w * dv)
+        a = scale * q[:, h] * ((wdv[0] - wdv[1]) @ k[:, kv])
+        var[kv] += np.sum(a ** 2)
     return 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass
 
 
@@ -142,6 +152,7 @@ def grad_tolerance_rows(q, k, v, dout, scale, S, R, kv_heads, rows_per_block=102
                 dd = np.asarray(dout[r0:r1, h], np.float64)
                 s = scale * np.asarray(q[r0:r1, h], np.float64) @ kk.T
                 causal = j <= i
+                wdv = []
                 for allowed in (causal, causal & ((j < S) | (i - j < R))):
                     z = np.where(allowed, s, -np.inf)
                     z -= z.max(axis=1, keepdims=True)
@@ -151,5 +162,8 @@ def grad_tolerance_rows(q, k, v, dout, scale, S, R, kv_heads, rows_per_block=102
                     dv = dd @ vv.T - np.sum(dd * o, axis=1, keepdims=True)
                     var += float(np.sum((w * dv) ** 2))
                     mass += float(np.sum(np.abs(dd * o)))
+                    wdv.append(w * dv)
+                a = scale * np.asarray(q[r0:r1, h], np.float64) * ((wdv[0] - wdv[1]) @ kk)
+                var += float(np.sum(a ** 2))
         out[kv] = 6.0 * 2.0 ** -9 * np.sqrt(var) + 1e-5 * mass
     return out
