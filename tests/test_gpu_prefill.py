@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from duo_synth import WORKLOADS, make_inputs
+from duo_synth import WORKLOADS, make_inputs, round_bf16
 from gpu_util import Routed, assert_blocks_close, device, say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -116,6 +116,20 @@ def test_prefill_short_window_no_sink(S, R):
     say(f"case: S={S} R={R}, chunks 130/170, then 2 decode steps")
     inp = make_inputs(w, tokens=300, steps=2, seed=7100 + 10 * S + R)
     _run_prefill(inp, [130, 170], decode_steps=2, label=f"S{S}R{R}")
+
+
+def test_prefill_rising_scores_rescale():
+    # key norms rising 1x -> 3x along the sequence: each query's scores grow
+    # tile after tile, so the running softmax reference moves up many times
+    # (the rescale path of the retrieval and streaming loops), from a first
+    # tile whose reference is taken fresh
+    w = dataclasses.replace(WORKLOADS["llama3_8b_prefill_64k"], n_q_heads=8, n_kv_heads=2,
+                            fixed_retrieval=(1,))
+    say("case: 640 tokens, key norms rising 1x..3x, chunks 256/384")
+    inp = make_inputs(w, tokens=640, seed=9100)
+    ramp = (1.0 + 2.0 * np.arange(640) / 640)[:, None, None]
+    inp.k = round_bf16(inp.k * ramp)
+    _run_prefill(inp, [256, 384], label="rising")
 
 
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (4, 64), (8, 128)])
