@@ -187,6 +187,11 @@ duo_status duo_append_kv(duo_layer* layer, const void* k, const void* v, int32_t
  * softmax weights; an INT4_G32 cache is attended in its decoded values
  * fma(code, scale, zero), rounded to fp16 (the chunk is quantised into the
  * cache first, so the chunk's own keys are decoded ones too).
+ * Retrieval heads over a 16-bit cache (and the gate-blended forward and its
+ * gate gradient below) take q multiplied by softmax_scale * log2(e) and
+ * rounded once to the product type, which costs accuracy when logits are
+ * large; DUO_EXACT_SCALE=1 in the environment, read at every launch, applies
+ * the scale in fp32 instead.
  * DUO_ERR_CAPACITY if n + chunk_len > capacity; DUO_ERR_UNSUPPORTED while the
  * sequences hold different counts (use duo_prefill_chunk_seq). */
 duo_status duo_prefill_chunk(duo_layer* layer, const void* q, const void* k, const void* v,

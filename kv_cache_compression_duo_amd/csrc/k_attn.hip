@@ -43,6 +43,7 @@
 //   * the next tile's loads are in flight while the current tile is
 //     computed; query tiles are launched longest-first (causal imbalance);
 //   * output rows leave through LDS as whole rows (coalesced stores).
+#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 
@@ -166,8 +167,18 @@ __device__ __forceinline__ const uint16_t* chunk_row(const AttnArgs& a, int b, i
 template <int MODE>
 constexpr int attn_waves() { return 8; }
 
-template <int D, int HB, int MODE>
-__global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnArgs a) {
+// Modes that can keep the softmax reference inside the QK product (q scaled
+// by scale * log2(e) and rounded once to the operand type); the others
+// always apply the scale in fp32.
+constexpr bool mode_prescale(int m) {
+  return m == MODE_RETRIEVAL || m == MODE_RETRIEVAL_F16 || m == MODE_MIXED ||
+         m == MODE_MIXED_BLOCK || m == MODE_GRAD || m == MODE_GRAD_BLOCK;
+}
+
+// PRE: the pre-scaled form above where the mode has it; false applies the
+// scale in fp32 (one FMA per score), exact for logits of any size.
+template <int D, int HB, int MODE, bool PRE>
+__device__ __forceinline__ void attn_body(AttnArgs a) {
   constexpr int NW = attn_waves<MODE>();
   constexpr int KS = D / 16;          // k-steps of the QK product
   constexpr int DB = D / 32;          // 32-row d-blocks of the PV product
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   // already is the exp2 argument (no FMA per score). The other modes stay
   // with raw scores: the streaming form has no 16 registers to spare, the
   // 4-bit form few.
-  constexpr bool kRel = (kCache && !kI4) || kTwoPhase;
+  constexpr bool kRel = PRE && mode_prescale(MODE);
   constexpr int KROW = kDma ? D : KPAD;  // K tile row stride in LDS (elements)
   // two LDS stages: tile k is read from stage k & 1 while tile k + 1 is
   // written to the other, so one barrier per tile suffices. The stages are
@@ -985,6 +996,22 @@ __global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnAr
   }
 }
 
+template <int D, int HB, int MODE>
+__global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel(AttnArgs a) {
+  attn_body<D, HB, MODE, true>(a);
+}
+template <int D, int HB, int MODE>
+__global__ __launch_bounds__(64 * attn_waves<MODE>(), 1) void attn_kernel_exact(AttnArgs a) {
+  attn_body<D, HB, MODE, false>(a);
+}
+
+// DUO_EXACT_SCALE=1 in the environment (read at every launch) selects the
+// fp32-scale form of the modes that otherwise pre-scale q.
+static bool exact_scale_requested() {
+  const char* e = getenv("DUO_EXACT_SCALE");
+  return e != nullptr && e[0] == '1';
+}
+
 // ---- launchers -------------------------------------------------------------------
 template <int D, int HB, int MODE>
 static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
@@ -1002,6 +1029,12 @@ static hipError_t launch_hb(const AttnArgs& a, int n_kv, int B, hipStream_t s) {
   x.tiles_in_y = !mode_streaming(MODE) && x.n_qtiles <= 65535;
   dim3 grid(x.tiles_in_y ? hgs : (unsigned)x.n_qtiles, x.tiles_in_y ? (unsigned)x.n_qtiles : hgs,
             (unsigned)B);
+  if constexpr (mode_prescale(MODE)) {
+    if (exact_scale_requested()) {
+      attn_kernel_exact<D, HB, MODE><<<grid, 64 * NW, 0, s>>>(x);
+      return hipGetLastError();
+    }
+  }
   attn_kernel<D, HB, MODE><<<grid, 64 * NW, 0, s>>>(x);
   return hipGetLastError();
 }

@@ -39,6 +39,12 @@ def test_mixed_llama2_ragged():
     _mixed(inp, inp.alpha, label=w.key)
 
 
+def test_mixed_llama2_ragged_exact_scale(monkeypatch):
+    # the fp32-scale form of the gate-blended forward (DUO_EXACT_SCALE=1)
+    monkeypatch.setenv("DUO_EXACT_SCALE", "1")
+    test_mixed_llama2_ragged()
+
+
 def test_mixed_llama2_full_length_sampled():
     w = WORKLOADS["llama2_7b_mixed_16k"]
     say(f"case: {w.key} T=16384, sampled rows")

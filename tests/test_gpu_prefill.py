@@ -132,6 +132,22 @@ def test_prefill_rising_scores_rescale():
     _run_prefill(inp, [256, 384], label="rising")
 
 
+def test_prefill_large_logits_exact_scale(monkeypatch):
+    # queries doubled and key norms rising 1x..3x: exp2 arguments spread over
+    # about 7 per query, where rounding q * scale * log2(e) to bf16 moves the
+    # outputs past the bar (max-abs about 0.027 in a float64 simulation);
+    # DUO_EXACT_SCALE=1 selects the form that applies the scale in fp32
+    monkeypatch.setenv("DUO_EXACT_SCALE", "1")
+    w = dataclasses.replace(WORKLOADS["llama3_8b_prefill_64k"], n_q_heads=8, n_kv_heads=2,
+                            fixed_retrieval=(1,))
+    say("case: 640 tokens, q x2, key norms rising 1x..3x, exact scale, chunks 256/384")
+    inp = make_inputs(w, tokens=640, seed=9100)
+    ramp = (1.0 + 2.0 * np.arange(640) / 640)[:, None, None]
+    inp.k = round_bf16(inp.k * ramp)
+    inp.q = round_bf16(inp.q * 2.0)
+    _run_prefill(inp, [256, 384], label="large logits, exact scale")
+
+
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (4, 64), (8, 128)])
 def test_prefill_group_sizes(G, D):
     w = dataclasses.replace(WORKLOADS["llama3_8b_prefill_64k"], n_q_heads=2 * G, n_kv_heads=2,
